@@ -1,0 +1,259 @@
+"""Plain, slow, fp64 reference for paged decode attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+bench's CPU-baseline leg; never by the product path.  It shares no code with
+the HIP library and reads the cache through its own logical layout.
+
+What it computes, and where the pages say so:
+  * Paged KV cache: the cache is split into fixed-size pages that are assigned
+    on demand; a decode step revisits every cached K/V of its sequence
+    ("How we built the most efficient inference engine for Cloudflare's
+    network", section "Batching to feed the Tensor Cores", KV-cache paragraph).
+  * Block table of integer page indices; one table per (sequence, head) lets
+    heads keep different numbers of tokens ("Making Workers AI faster and more
+    efficient" -- KV cache compression page, section "KV cache compression goes
+    open source", the block-table paragraph).
+  * FP8 e4m3 KV cache instead of BF16 ("Cloudflare quantizes Kimi and GLM
+    caches for 41% faster inference", KV cache quantization paragraph).
+  * Page-tag integrity check: each physical page carries a tag that changes on
+    reallocation; the server records the (page, tag) pairs a request expects;
+    the pairs are checked in a separate batch validation before decode reads
+    the cache, and a mismatch aborts the request (same page, integrity-check
+    paragraph).
+
+Readings taken where the pages are silent (each is also in the design notes):
+  R1 Logical layout: SEQ pools are [P][Hkv][S][D] with a [B][W] table and [B]
+     lengths; HEAD pools are [P][S][D] with a [B][Hkv][W] table and [B][Hkv]
+     lengths.  Token t of a unit lives at page table[t // S], slot t % S.
+  R2 FP8 scales: one fp32 scale per (physical page, KV head), separate for K
+     and V, kept equal to fl32(amax / 448) over every value written to that
+     page-head since the page was last started fresh.
+  R3 Quantisation: code = e4m3_rne_sat(fl32(x / s)); fl32 is IEEE binary32
+     division (numpy float32), then an exact round-to-nearest-even.
+  R4 Appending into a partly filled page: when the new values raise the scale
+     from s_old to s_new, the codes already in the page are re-quantised as
+     e4m3_rne_sat(fl32(fl32(dec(c) * s_old) / s_new)).  A page whose first
+     written slot in a call is slot 0 is fresh: its old scale is ignored.
+  R5 Append never checks tags; it still refuses out-of-range page ids (flag
+     bit 1) and writes past table_width * S (flag bit 2).
+  R6 Validation flags, per sequence b, OR-ed over its units: bit 0 a tag
+     mismatch, bit 1 a page id outside [0, P) (its tag is then not compared),
+     bit 2 a length above table_width * S (entries checked up to the width).
+     Only the ceil(L / S) entries a decode would read are checked.
+  R7 Decode: query head hq uses KV head hq // (Hq / Hkv); scores are
+     sigma * q . k over all L tokens; softmax with the max subtracted; a
+     flagged sequence, or a unit with L = 0, yields exact zeros.
+"""
+import numpy as np
+
+from .codecs import (
+    bf16_to_f64,
+    e4m3_from_f32_rne_sat,
+    e4m3_to_f64,
+)
+
+FLAG_TAG_MISMATCH = 1
+FLAG_PAGE_OOB = 2
+FLAG_LEN_OVERFLOW = 4
+E4M3_MAX_F32 = np.float32(448.0)
+
+
+class OracleCache:
+    """Logical cache state: pools indexed [page][head][slot][dim].
+
+    HEAD layout pools carry a head axis of length 1 so that both layouts share
+    one indexing rule inside the oracle.
+    """
+
+    def __init__(self, layout, kv_dtype, num_pages, page_size, num_kv_heads, head_dim):
+        assert layout in ("seq", "head") and kv_dtype in ("bf16", "fp8")
+        self.layout, self.kv_dtype = layout, kv_dtype
+        self.P, self.S, self.Hkv, self.D = num_pages, page_size, num_kv_heads, head_dim
+        ph = num_kv_heads if layout == "seq" else 1
+        if kv_dtype == "bf16":
+            self.k = np.full((num_pages, ph, page_size, head_dim), 0x7FC0, np.uint16)
+            self.v = np.full_like(self.k, 0x7FC0)
+            self.k_scale = self.v_scale = None
+        else:
+            self.k = np.full((num_pages, ph, page_size, head_dim), 0x7F, np.uint8)
+            self.v = np.full_like(self.k, 0x7F)
+            self.k_scale = np.full((num_pages, ph), np.nan, np.float32)
+            self.v_scale = np.full((num_pages, ph), np.nan, np.float32)
+
+    def copy(self):
+        c = OracleCache.__new__(OracleCache)
+        c.__dict__.update(self.__dict__)
+        c.k, c.v = self.k.copy(), self.v.copy()
+        if self.k_scale is not None:
+            c.k_scale, c.v_scale = self.k_scale.copy(), self.v_scale.copy()
+        return c
+
+
+def units(layout, batch, num_kv_heads):
+    """(b, kv head, table-row index, pool head index) for every attention unit.
+
+    SEQ: one table row per sequence, shared by all KV heads.
+    HEAD: one table row per (sequence, KV head); the pool has no head axis.
+    """
+    out = []
+    for b in range(batch):
+        for h in range(num_kv_heads):
+            if layout == "seq":
+                out.append((b, h, (b,), h))
+            else:
+                out.append((b, h, (b, h), 0))
+    return out
+
+
+# --------------------------------------------------------------- append
+def _quantise(values_f32, scale):
+    """R3: codes of fp32 values under one fp32 scale (scale 0 -> all +0)."""
+    if scale == 0:
+        return np.zeros(values_f32.shape, np.uint8)
+    q = (values_f32.astype(np.float32) / np.float32(scale)).astype(np.float32)
+    return e4m3_from_f32_rne_sat(q)
+
+
+def _append_fp8_page(pool, scales, pid, ph, first_slot, slots, new_bits):
+    """R2/R4 for one (page, head) and one of K or V.
+
+    new_bits: bf16 bit patterns [len(slots)][D] written at `slots`, which are
+    consecutive and start at first_slot.
+    """
+    x = bf16_to_f64(new_bits).astype(np.float32)        # exact: bf16 is a subset of fp32
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s_cand = np.float32(amax / E4M3_MAX_F32)            # fl32(amax / 448)
+    s_old = np.float32(0) if first_slot == 0 else scales[pid, ph]
+    s_new = max(s_old, s_cand)
+    if s_new > s_old and first_slot > 0:
+        old = e4m3_to_f64(pool[pid, ph, :first_slot]).astype(np.float32)   # exact
+        back = (old * s_old).astype(np.float32)          # fl32(dec(c) * s_old)
+        pool[pid, ph, :first_slot] = _quantise(back, s_new)
+    pool[pid, ph, slots] = _quantise(x, s_new)
+    scales[pid, ph] = s_new
+
+
+def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width):
+    """Write n_new[u] tokens per unit at positions lens_old[u] ... .
+
+    block_table: int32 [B][W] (SEQ) or [B][Hkv][W] (HEAD)
+    lens_old, n_new: int32 [B] (SEQ) or [B][Hkv] (HEAD)
+    k_new, v_new: bf16 bits uint16 [B][Hkv][n_max][D]
+    Updates `cache` in place and returns the per-sequence flags (uint32 [B]).
+    """
+    c = cache
+    B, Hkv = k_new.shape[0], k_new.shape[1]
+    S, W, P = c.S, table_width, c.P
+    flags = np.zeros(B, np.uint32)
+    for (b, h, row, ph) in units(c.layout, B, Hkv):
+        table = block_table[row]
+        pos0, n = int(lens_old[row]), int(n_new[row])
+        if pos0 + n > W * S:
+            flags[b] |= FLAG_LEN_OVERFLOW
+        n_ok = max(0, min(pos0 + n, W * S) - pos0)
+        t = 0
+        while t < n_ok:                       # one page at a time
+            pos = pos0 + t
+            i, slot0 = pos // S, pos % S
+            cnt = min(S - slot0, n_ok - t)
+            pid = int(table[i])
+            if not (0 <= pid < P):
+                flags[b] |= FLAG_PAGE_OOB
+                t += cnt
+                continue
+            slots = np.arange(slot0, slot0 + cnt)
+            for pool, scales, src in ((c.k, c.k_scale, k_new), (c.v, c.v_scale, v_new)):
+                bits = src[b, h, t:t + cnt]
+                if c.kv_dtype == "bf16":
+                    pool[pid, ph, slots] = bits
+                else:
+                    _append_fp8_page(pool, scales, pid, ph, slot0, slots, bits)
+            t += cnt
+    return flags
+
+
+# ------------------------------------------------------------- validate
+def oracle_validate(layout, num_pages, page_size, block_table, lens, page_tags,
+                    expected_tags, table_width):
+    """R6.  expected_tags None is the no-op tracker: only bits 1 and 2."""
+    B = block_table.shape[0]
+    Hkv = 1 if layout == "seq" else block_table.shape[1]
+    flags = np.zeros(B, np.uint32)
+    for (b, h, row, _) in units(layout, B, Hkv):
+        L = int(lens[row])
+        if L > table_width * page_size:
+            flags[b] |= FLAG_LEN_OVERFLOW
+        n_pages = -(-min(L, table_width * page_size) // page_size)
+        for i in range(n_pages):
+            pid = int(block_table[row][i])
+            if not (0 <= pid < num_pages):
+                flags[b] |= FLAG_PAGE_OOB
+            elif expected_tags is not None and expected_tags[row][i] != page_tags[pid]:
+                flags[b] |= FLAG_TAG_MISMATCH
+    return flags
+
+
+# --------------------------------------------------------------- decode
+def gather_unit(cache, table_row, ph, L):
+    """K-hat, V-hat of one unit as dense fp64 [L][D] (the M x N view of one head)."""
+    S = cache.S
+    n_pages = -(-L // S)
+    pages = np.asarray(table_row[:n_pages], dtype=np.int64)
+    kb = cache.k[pages, ph].reshape(n_pages * S, cache.D)[:L]
+    vb = cache.v[pages, ph].reshape(n_pages * S, cache.D)[:L]
+    if cache.kv_dtype == "bf16":
+        return bf16_to_f64(kb), bf16_to_f64(vb)
+    ks = np.repeat(cache.k_scale[pages, ph].astype(np.float64), S)[:L]
+    vs = np.repeat(cache.v_scale[pages, ph].astype(np.float64), S)[:L]
+    return e4m3_to_f64(kb) * ks[:, None], e4m3_to_f64(vb) * vs[:, None]
+
+
+def attention_f64(q, K, V, sigma):
+    """Textbook single-query softmax attention in fp64: returns (o, weights)."""
+    z = float(sigma) * (K @ q)
+    w = np.exp(z - z.max())
+    w = w / w.sum()
+    return w @ V, w
+
+
+def oracle_decode_row(cache, q_bits, table_row, L, ph, sigma):
+    """One output row o[D] for one query head (bf16 bits q_bits[D])."""
+    if L == 0:
+        return np.zeros(cache.D)
+    K, V = gather_unit(cache, table_row, ph, L)
+    o, _ = attention_f64(bf16_to_f64(q_bits), K, V, sigma)
+    return o
+
+
+def oracle_decode(cache, q, block_table, lens, sigma, flags=None):
+    """out[b][hq][:] in fp64 for q bf16 bits [B][Hq][D]."""
+    B, Hq, D = q.shape
+    G = Hq // cache.Hkv
+    out = np.zeros((B, Hq, D))
+    for (b, h, row, ph) in units(cache.layout, B, cache.Hkv):
+        if flags is not None and flags[b] != 0:
+            continue
+        L = int(lens[row])
+        if L == 0:
+            continue
+        K, V = gather_unit(cache, block_table[row], ph, L)
+        for g in range(G):
+            hq = h * G + g
+            out[b, hq], _ = attention_f64(bf16_to_f64(q[b, hq]), K, V, sigma)
+    return out
+
+
+def lse_partial(q, K, V, sigma):
+    """(m, l, o_unnormalised) of one token subset, natural-log domain, fp64."""
+    z = float(sigma) * (K @ q)
+    m = z.max()
+    p = np.exp(z - m)
+    return m, p.sum(), p @ V
+
+
+def lse_merge(parts):
+    """Merge (m, l, o) partials of disjoint token subsets into the softmax output."""
+    M = max(m for m, _, _ in parts)
+    Lsum = sum(l * np.exp(m - M) for m, l, _ in parts)
+    O = sum(o * np.exp(m - M) for m, _, o in parts)
+    return O / Lsum
