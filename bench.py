@@ -1,0 +1,284 @@
+"""Benchmark of one paged-decode step on one MI355X.
+
+A step is the whole hot path for one batch: pa_cache_append of the step's new
+token for every (sequence, KV head), then pa_decode (page-tag validation,
+split-K attention, partition reduce).  Inputs are synthetic and seeded
+(decode_attention_paged_pa_amd.workloads) and resident in HBM before timing.
+
+Default workload: the 70B-shaped FP8 layer, B 64, 64 query / 8 KV heads,
+D 128, 32768 tokens per sequence (4.29 GB of FP8 KV), split-K 8, tag check on.
+
+Timing: W untimed warm-up steps; then K steps, each preceded (outside the
+timed events) by a 512 MiB write that evicts L2 and the Infinity Cache; HIP
+events on the launch stream bracket the step and each kernel.  The K steps
+are also bracketed by device synchronisation for a wall-clock figure.
+
+Prints one JSON line.  `value` is the achieved HBM GB/s of the step
+(algorithmic bytes / mean step time); `roofline` is the attention kernel
+against the 8 TB/s HBM peak; `cpu_baseline` is the fp64 oracle's decode on a
+bounded sample of the same workload, on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, check=True):
+    """Bytes the method must move for one decode step (append + decode).
+
+    Decode: every attended token's K and V once (L x Hkv_u x D x 2 x e), Q in and
+    O out (BF16), one table entry per page read, FP8 scales per (page, head),
+    and with the check on the expected and current tag per page plus the flags.
+    Append: the new token's BF16 K/V in and its cached K/V out.
+    """
+    import numpy as np
+
+    e = 1 if w.kv_dtype == "fp8" else 2
+    L = w.lens.astype(np.int64)
+    hkv_u = w.Hkv if w.layout == "seq" else 1
+    pages = (-(-L // w.S)).sum()
+    kv = int(L.sum()) * hkv_u * w.D * 2 * e
+    qo = 2 * w.B * w.Hq * w.D * 2
+    table = 4 * int(pages)
+    scales = 8 * int(pages) * hkv_u if e == 1 else 0
+    tags = (8 * int(pages) + 4 * w.B) if check else 0
+    n_units = w.B * w.Hkv
+    append = n_units * w.D * 2 * (2 + e)
+    attn = kv + w.B * w.Hq * w.D * 2 + table + scales
+    return dict(kv=kv, decode=kv + qo + table + scales + tags, append=append,
+                step=kv + qo + table + scales + tags + append, attention_kernel=attn)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h"):
+        with open(os.path.join(ROOT, "decode_attention_paged_pa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name, per_launch_units):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_attention_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU baseline
+def _oracle_worker(w, seqs, barrier, queue):
+    import numpy as np  # noqa: F401
+
+    from oracle import oracle_decode
+    from tests.oracle_fill import oracle_fill
+
+    cache, _ = oracle_fill(w, seqs=seqs)           # untimed: building the cache
+    barrier.wait()
+    t0 = time.perf_counter()
+    for b in seqs:
+        oracle_decode(cache, w.q[b:b + 1], w.block_table[b:b + 1], w.lens[b:b + 1], w.sigma)
+    queue.put(time.perf_counter() - t0)
+
+
+def cpu_baseline(w, n_seqs):
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), n_seqs))
+    step = max(1, w.B // n_seqs)
+    sample = list(range(0, w.B, step))[:n_seqs]
+    shares = [sample[i::cores] for i in range(cores)]
+    barrier = ctx.Barrier(cores + 1)
+    queue = ctx.Queue()
+    env_threads = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                    "MKL_NUM_THREADS")}
+    for k in env_threads:
+        os.environ[k] = "1"
+    procs = [ctx.Process(target=_oracle_worker, args=(w, s, barrier, queue)) for s in shares]
+    for p in procs:
+        p.start()
+    for k, v in env_threads.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+    barrier.wait()
+    t0 = time.perf_counter()
+    times = [queue.get(timeout=600) for _ in procs]
+    wall = time.perf_counter() - t0
+    for p in procs:
+        p.join()
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except Exception:
+        pass
+    return dict(value=len(sample) / wall, unit="tokens/s", cores=cores, kind="oracle",
+                sample="oracle_decode (gather, FP8 dequant, fp64 attention) of %d of the %d "
+                       "sequences (all %d query heads each) of the same workload, one per worker, "
+                       "cache build untimed; %.1f s of CPU decode work; %s" % (
+                           len(sample), w.B, w.Hq, sum(times), cpu_model),
+                seconds_wall=wall)
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, help="workload 2..5")
+    ap.add_argument("--partitions", type=int, default=-1, help="split-K count (-1: 8 for workload 5, else auto)")
+    ap.add_argument("--no-check", action="store_true", help="no-op tracker: skip the tag check")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threads", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_paged_pa_amd import pa
+    from decode_attention_paged_pa_amd.device_inputs import build_device_workload
+    from decode_attention_paged_pa_amd.workloads import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args.config, stale_frac=0.0)
+    parts = args.partitions if args.partitions >= 0 else (8 if args.config == 5 else 0)
+    check = not args.no_check
+    log("workload %d %s: B=%d Hq=%d Hkv=%d D=%d kv=%s layout=%s tokens=%d" % (
+        w.cfg_id, w.name, w.B, w.Hq, w.Hkv, w.D, w.kv_dtype, w.layout, int(w.lens.sum())))
+    t0 = time.time()
+    dw = build_device_workload(w, device=dev, threads=args.threads, log=log)
+    dw.step_append()
+    torch.cuda.synchronize()
+    log("cache filled in %.1f s" % (time.time() - t0))
+    n_parts = pa.num_partitions(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
+    ws_bytes = pa.workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        dw.step_append()
+        dw.decode(check=check, num_partitions=parts, out=out, workspace=workspace,
+                  events=None if evs is None else evs[1:])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for e in evs:
+        for x in e:
+            x.record(stream)   # create the underlying events before timing
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        if not args.no_flush:
+            flush.zero_()
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_step = np.array([e[0].elapsed_time(e[4]) for e in evs])          # ms
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_val = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_attn = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    t_red = np.array([e[3].elapsed_time(e[4]) for e in evs])
+    ms = float(t_step.mean())
+    by = algorithmic_bytes(w, check)
+    gbs = by["step"] / (ms * 1e-3) / 1e9
+    attn_gbs = by["attention_kernel"] / (t_attn.mean() * 1e-3) / 1e9
+    tok_s = w.B / (ms * 1e-3)
+    log("step %.3f ms (p10 %.3f p90 %.3f); append %.1f us, validate %.1f us, attention %.1f us, "
+        "reduce %.1f us; %.0f GB/s step, attention %.0f GB/s (%.1f%% of 8 TB/s)" % (
+            ms, np.percentile(t_step, 10), np.percentile(t_step, 90), t_append.mean() * 1e3,
+            t_val.mean() * 1e3, t_attn.mean() * 1e3, t_red.mean() * 1e3, gbs, attn_gbs,
+            100 * attn_gbs / HBM_PEAK_GBS))
+
+    traffic = traffic_from_profile(w.name, None)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: B=%d, Hq=%d, Hkv=%d, D=%d, page 16, L=%s, %s KV, %s layout, "
+                        "split-K %d, tag check %s" % (
+                            w.name, w.B, w.Hq, w.Hkv, w.D,
+                            "32768" if args.config == 5 else "drawn",
+                            "FP8 e4m3" if w.kv_dtype == "fp8" else "BF16", w.layout.upper(),
+                            n_parts, "on" if check else "off"),
+            "global_batch": w.B,
+            "tokens_attended": int(w.lens.sum()),
+            "parallelism": "1 GPU",
+        },
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tok_s, 1),
+        "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
+        "kernels_us": {"append": round(t_append.mean() * 1e3, 2),
+                       "validate": round(t_val.mean() * 1e3, 2),
+                       "attention": round(t_attn.mean() * 1e3, 2),
+                       "reduce": round(t_red.mean() * 1e3, 2)},
+        "algorithmic_bytes": by,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attention_kernel",
+            "achieved": round(attn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    del flush, workspace
+    if not args.no_cpu_baseline:
+        log("timing the oracle on %d sequences ..." % args.cpu_seqs)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+        log("oracle: %.3f tokens/s on %d cores" % (result["cpu_baseline"]["value"],
+                                                  result["cpu_baseline"]["cores"]))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+// C-ABI entry points of libpa: argument checks, partition choice, workspace
+// sizing and kernel launches.  Declarations and contracts are in pa.h.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa_internal.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_cache(const pa_cache_desc* c) {
+  if (!c) return PA_ERR_INVALID_ARG;
+  if (c->layout != PA_LAYOUT_SEQ && c->layout != PA_LAYOUT_HEAD) return PA_ERR_INVALID_ARG;
+  if (c->kv_dtype != PA_KV_BF16 && c->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (c->page_size != pa::kPageSize) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!c->k_pages || !c->v_pages) return PA_ERR_INVALID_ARG;
+  if (!aligned(c->k_pages, 256) || !aligned(c->v_pages, 256)) return PA_ERR_INVALID_ARG;
+  if (c->kv_dtype == PA_KV_FP8_E4M3) {
+    if (!c->k_scale || !c->v_scale) return PA_ERR_INVALID_ARG;
+    if (!aligned(c->k_scale, 4) || !aligned(c->v_scale, 4)) return PA_ERR_INVALID_ARG;
+  }
+  return PA_OK;
+}
+
+int check_seq(const pa_seq_desc* s) {
+  if (!s) return PA_ERR_INVALID_ARG;
+  if (s->batch <= 0 || s->table_width <= 0) return PA_ERR_INVALID_ARG;
+  if ((int64_t)s->table_width * pa::kPageSize > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (!s->block_table || !s->lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(s->block_table, 4) || !aligned(s->lens, 4)) return PA_ERR_INVALID_ARG;
+  if (s->expected_tags && !aligned(s->expected_tags, 4)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int check_heads(const pa_cache_desc* c, int32_t num_q_heads) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_q_heads / c->num_kv_heads > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+size_t elem_bytes(const pa_cache_desc* c) { return c->kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
+
+// Token partitioning of each unit: partitions are runs of chunk_pages pages.
+// Automatic choice: enough workgroups to cover the 256 compute units several
+// times at the table's capacity, with at least 32 pages (8 per wave) and at
+// most 256 pages per workgroup.
+void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req,
+                       int* chunk_pages, int* num_parts) {
+  const int W = s->table_width;
+  int cp;
+  if (req > 0) {
+    cp = (W + req - 1) / req;
+  } else {
+    const int64_t units = (int64_t)s->batch * c->num_kv_heads;
+    const int64_t target = 2048;
+    int64_t x = (units * W + target - 1) / target;
+    if (x < 32) x = 32;
+    if (x > 256) x = 256;
+    cp = (int)x;
+  }
+  if (cp > W) cp = W;
+  if (cp < 1) cp = 1;
+  *chunk_pages = cp;
+  *num_parts = (W + cp - 1) / cp;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int parts) {
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)s->batch * hq * parts;
+  return align256(rows * c->head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
+                const uint16_t* q, uint16_t* out, float softmax_scale, int32_t num_partitions,
+                uint32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                pa_event_t const* events) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  if ((rc = check_heads(cache, num_q_heads)) != PA_OK) return rc;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return PA_ERR_INVALID_ARG;
+  if (num_partitions < 0) return PA_ERR_INVALID_ARG;
+  if (seq->expected_tags && (!flags || !cache->page_tags)) return PA_ERR_INVALID_ARG;
+  if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
+  int chunk_pages, parts;
+  choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts);
+  const size_t need = workspace_for(cache, seq, num_q_heads, parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PA_ERR_WORKSPACE;
+  const bool head = cache->layout == PA_LAYOUT_HEAD;
+  const bool fp8 = cache->kv_dtype == PA_KV_FP8_E4M3;
+
+  auto rec = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), stream);
+  };
+
+  rec(0);
+  if (flags) {
+    pa::ValidateArgs v{};
+    v.block_table = seq->block_table;
+    v.lens = seq->lens;
+    v.expected_tags = seq->expected_tags;
+    v.page_tags = cache->page_tags;
+    v.flags = flags;
+    v.batch = seq->batch;
+    v.num_kv_heads = cache->num_kv_heads;
+    v.table_width = seq->table_width;
+    v.num_pages = cache->num_pages;
+    v.head_layout = head;
+    if (pa::launch_validate(v, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  rec(1);
+
+  pa::AttnArgs a{};
+  a.k_pages = static_cast<const uint8_t*>(cache->k_pages);
+  a.v_pages = static_cast<const uint8_t*>(cache->v_pages);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = seq->block_table;
+  a.lens = seq->lens;
+  a.flags = flags;
+  a.q = q;
+  a.out = out;
+  if (parts > 1) {
+    const size_t rows = (size_t)seq->batch * num_q_heads * parts;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256(rows * cache->head_dim * sizeof(float)));
+  }
+  a.batch = seq->batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.table_width = seq->table_width;
+  a.num_pages = cache->num_pages;
+  a.chunk_pages = chunk_pages;
+  a.num_parts = parts;
+  a.score_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  if (pa::launch_attention(a, cache->head_dim, fp8, head, stream) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  rec(2);
+  if (parts > 1) {
+    if (pa::launch_reduce(a, cache->head_dim, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  rec(3);
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_API size_t pa_pool_bytes(const pa_cache_desc* c) {
+  if (!c || c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0 || c->head_dim <= 0)
+    return 0;
+  if (c->kv_dtype != PA_KV_BF16 && c->kv_dtype != PA_KV_FP8_E4M3) return 0;
+  const size_t heads = c->layout == PA_LAYOUT_SEQ ? (size_t)c->num_kv_heads : 1;
+  return (size_t)c->num_pages * heads * c->page_size * c->head_dim * elem_bytes(c);
+}
+
+PA_API int pa_cache_append(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                           const int32_t* n_new, int32_t n_max, const uint16_t* k_new,
+                           const uint16_t* v_new, uint32_t* flags, pa_stream_t stream) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  if (!n_new || !aligned(n_new, 4) || n_max < 0) return PA_ERR_INVALID_ARG;
+  if (n_max == 0) {
+    if (!flags) return PA_OK;
+  } else if (!k_new || !v_new || !aligned(k_new, 2) || !aligned(v_new, 2)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
+  pa::AppendArgs a{};
+  a.k_pages = static_cast<uint8_t*>(cache->k_pages);
+  a.v_pages = static_cast<uint8_t*>(cache->v_pages);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = seq->block_table;
+  a.lens_old = seq->lens;
+  a.n_new = n_new;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.flags = flags;
+  a.batch = seq->batch;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.table_width = seq->table_width;
+  a.num_pages = cache->num_pages;
+  a.n_max = n_max;
+  a.pages_per_unit = n_max == 0 ? 0 : (n_max + pa::kPageSize - 1) / pa::kPageSize + 1;
+  a.head_layout = cache->layout == PA_LAYOUT_HEAD;
+  a.fp8 = cache->kv_dtype == PA_KV_FP8_E4M3;
+  const int64_t grid = (int64_t)a.batch * a.num_kv_heads * a.pages_per_unit;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (pa::launch_append(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                        int32_t num_q_heads, int32_t num_partitions) {
+  if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
+      check_heads(cache, num_q_heads) != PA_OK || num_partitions < 0)
+    return (size_t)-1;
+  int cp, parts;
+  choose_partitions(cache, seq, num_partitions, &cp, &parts);
+  return workspace_for(cache, seq, num_q_heads, parts);
+}
+
+PA_API int pa_decode_num_partitions(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                    int32_t num_q_heads, int32_t num_partitions) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  if ((rc = check_heads(cache, num_q_heads)) != PA_OK) return rc;
+  if (num_partitions < 0) return PA_ERR_INVALID_ARG;
+  int cp, parts;
+  choose_partitions(cache, seq, num_partitions, &cp, &parts);
+  return parts;
+}
+
+PA_API int pa_decode(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
+                     const uint16_t* q, uint16_t* out, float softmax_scale,
+                     int32_t num_partitions, uint32_t* flags, void* workspace,
+                     size_t workspace_bytes, pa_stream_t stream) {
+  return decode_impl(cache, seq, num_q_heads, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+PA_API int pa_decode_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                           int32_t num_q_heads, const uint16_t* q, uint16_t* out,
+                           float softmax_scale, int32_t num_partitions, uint32_t* flags,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream,
+                           pa_event_t const events[4]) {
+  return decode_impl(cache, seq, num_q_heads, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events);
+}
+
+PA_API const char* pa_strerror(int code) {
+  switch (code) {
+    case PA_OK: return "success";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape (page_size 16, head_dim 64/128, group <= 16)";
+    case PA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+PA_API int pa_version(void) { return kVersion; }

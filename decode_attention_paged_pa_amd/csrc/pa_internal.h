@@ -1,0 +1,63 @@
+// Internal declarations shared by the kernels and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kPageSize = 16;      // tokens per page (S)
+constexpr int kWaves = 4;          // waves per attention workgroup
+constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
+
+// Arguments of the attention (partial) kernel.
+struct AttnArgs {
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const float* k_scale;      // FP8 only
+  const float* v_scale;      // FP8 only
+  const int32_t* block_table;
+  const int32_t* lens;
+  const uint32_t* flags;     // nullptr: nothing flagged
+  const uint16_t* q;
+  uint16_t* out;             // written directly when num_parts == 1
+  float* part_o;             // [B][Hq][Pn][D] unnormalised outputs
+  float* part_ml;            // [B][Hq][Pn][2] running max (log2 domain) and sum
+  int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
+  int chunk_pages, num_parts;
+  float score_scale_log2;    // softmax_scale * log2(e)
+};
+
+struct ValidateArgs {
+  const int32_t* block_table;
+  const int32_t* lens;
+  const uint32_t* expected_tags;  // nullptr: range and length checks only
+  const uint32_t* page_tags;
+  uint32_t* flags;
+  int batch, num_kv_heads, table_width, num_pages;
+  bool head_layout;
+};
+
+struct AppendArgs {
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  float* k_scale;
+  float* v_scale;
+  const int32_t* block_table;
+  const int32_t* lens_old;
+  const int32_t* n_new;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint32_t* flags;
+  int batch, num_kv_heads, head_dim, table_width, num_pages, n_max;
+  int pages_per_unit;         // ceil(n_max / S) + 1: grid slots per unit
+  bool head_layout, fp8;
+};
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,
+                            hipStream_t s);
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,267 @@
+"""Python binding of libpa (ctypes): argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels of libpa.so; this module
+checks tensor dtypes, shapes and devices, passes raw device pointers and the
+current HIP stream, and turns negative return codes into exceptions.  It has
+no CPU fallback: without the built library every call raises.
+
+Entry points mirror include/pa.h: append (pa_cache_append), decode
+(pa_decode / pa_decode_timed), workspace_bytes, num_partitions, pool_bytes.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
+
+LAYOUT = {"seq": 0, "head": 1}
+KV_DTYPE = {"bf16": 0, "fp8": 1}
+PAGE_SIZE = 16
+
+PA_FLAG_TAG_MISMATCH = 1
+PA_FLAG_PAGE_OOB = 2
+PA_FLAG_LEN_OVERFLOW = 4
+
+
+class PAError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("%s failed: %s (%d)" % (what, _strerror(code), code))
+        self.code = code
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("page_tags", ctypes.c_void_p),
+    ]
+
+
+class SeqDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("table_width", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("lens", ctypes.c_void_p),
+        ("expected_tags", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libpa.so (torch's HIP runtime is loaded first so both share it)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpa.so is not built (%s); run "
+                               "`python -m decode_attention_paged_pa_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.pa_pool_bytes.argtypes = [P(CacheDesc)]
+        L.pa_pool_bytes.restype = sz
+        L.pa_cache_append.argtypes = [P(CacheDesc), P(SeqDesc), vp, i32, vp, vp, vp, vp]
+        L.pa_cache_append.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32]
+        L.pa_decode_workspace_bytes.restype = sz
+        L.pa_decode_num_partitions.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32]
+        L.pa_decode_num_partitions.restype = ctypes.c_int
+        L.pa_decode.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float, i32, vp,
+                                vp, sz, vp]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_timed.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float, i32,
+                                      vp, vp, sz, vp, P(vp)]
+        L.pa_decode_timed.restype = ctypes.c_int
+        L.pa_strerror.argtypes = [ctypes.c_int]
+        L.pa_strerror.restype = ctypes.c_char_p
+        L.pa_version.argtypes = []
+        L.pa_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _strerror(code):
+    try:
+        return lib().pa_strerror(code).decode()
+    except Exception:  # library missing: still report the code
+        return "error"
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtypes, device=True):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if device and t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+I32 = (torch.int32,)
+U32 = (torch.int32, torch.uint32)
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+class PagedKVCache:
+    """The physical cache: K/V pools (raw bytes), FP8 scales and page tags.
+
+    Pools are allocated with the byte size pa_pool_bytes reports and filled with
+    NaN patterns (0x7FC0 for BF16, 0x7F for FP8) so that a read of an unwritten
+    slot shows up in the results.
+    """
+
+    def __init__(self, layout, kv_dtype, num_pages, num_kv_heads, head_dim, device="cuda",
+                 page_tags=None, poison=True):
+        self.layout, self.kv_dtype = layout, kv_dtype
+        self.num_pages, self.num_kv_heads, self.head_dim = int(num_pages), int(num_kv_heads), int(head_dim)
+        self.page_size = PAGE_SIZE
+        d = CacheDesc(LAYOUT[layout], KV_DTYPE[kv_dtype], self.num_pages, PAGE_SIZE,
+                      self.num_kv_heads, self.head_dim, None, None, None, None, None)
+        nbytes = lib().pa_pool_bytes(ctypes.byref(d))
+        if nbytes == 0:
+            raise ValueError("invalid cache shape")
+        self.pool_bytes = nbytes
+        self.k = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.v = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        heads = self.num_kv_heads if layout == "seq" else 1
+        if kv_dtype == "fp8":
+            self.k_scale = torch.full((self.num_pages, heads), float("nan"), dtype=torch.float32, device=device)
+            self.v_scale = torch.full_like(self.k_scale, float("nan"))
+        else:
+            self.k_scale = self.v_scale = None
+        if poison:
+            if kv_dtype == "bf16":
+                self.k.view(torch.int16).fill_(0x7FC0)
+                self.v.view(torch.int16).fill_(0x7FC0)
+            else:
+                self.k.fill_(0x7F)
+                self.v.fill_(0x7F)
+        self.page_tags = None if page_tags is None else _need(page_tags, "page_tags", U32)
+
+    def desc(self):
+        return CacheDesc(LAYOUT[self.layout], KV_DTYPE[self.kv_dtype], self.num_pages, PAGE_SIZE,
+                         self.num_kv_heads, self.head_dim, _ptr(self.k), _ptr(self.v),
+                         _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.page_tags))
+
+
+def _seq(cache, block_table, lens, expected_tags=None):
+    _need(block_table, "block_table", I32)
+    _need(lens, "lens", I32)
+    if cache.layout == "seq":
+        if block_table.dim() != 2 or lens.dim() != 1 or lens.shape[0] != block_table.shape[0]:
+            raise ValueError("SEQ layout expects block_table [B][W] and lens [B]")
+    else:
+        if (block_table.dim() != 3 or block_table.shape[1] != cache.num_kv_heads
+                or tuple(lens.shape) != tuple(block_table.shape[:2])):
+            raise ValueError("HEAD layout expects block_table [B][Hkv][W] and lens [B][Hkv]")
+    if expected_tags is not None:
+        _need(expected_tags, "expected_tags", U32)
+        if tuple(expected_tags.shape) != tuple(block_table.shape):
+            raise ValueError("expected_tags must have the block table's shape")
+    return SeqDesc(block_table.shape[0], block_table.shape[-1], _ptr(block_table), _ptr(lens),
+                   _ptr(expected_tags))
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def append(cache, block_table, lens, n_new, k_new, v_new, flags=None, stream=None):
+    """pa_cache_append: write n_new[u] tokens of k_new/v_new [B][Hkv][n_max][D] (BF16)."""
+    sd = _seq(cache, block_table, lens)
+    _need(n_new, "n_new", I32)
+    if tuple(n_new.shape) != tuple(lens.shape):
+        raise ValueError("n_new must have the shape of lens")
+    _need(k_new, "k_new", BF16)
+    _need(v_new, "v_new", BF16)
+    B = block_table.shape[0]
+    if (k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B
+            or k_new.shape[1] != cache.num_kv_heads or k_new.shape[3] != cache.head_dim):
+        raise ValueError("k_new/v_new must be [B][Hkv][n_max][D]")
+    if flags is not None:
+        _need(flags, "flags", U32)
+        if flags.numel() != B:
+            raise ValueError("flags must hold B words")
+    cd = cache.desc()
+    rc = lib().pa_cache_append(ctypes.byref(cd), ctypes.byref(sd), _ptr(n_new), k_new.shape[2],
+                               _ptr(k_new), _ptr(v_new), _ptr(flags), _stream(stream))
+    if rc != 0:
+        raise PAError(rc, "pa_cache_append")
+
+
+def workspace_bytes(cache, block_table, lens, num_q_heads, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_decode_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                        num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(-1, "pa_decode_workspace_bytes")
+    return n
+
+
+def num_partitions(cache, block_table, lens, num_q_heads, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_decode_num_partitions(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                       num_partitions)
+    if n < 0:
+        raise PAError(n, "pa_decode_num_partitions")
+    return n
+
+
+def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
+           num_partitions=0, out=None, workspace=None, events=None, stream=None):
+    """pa_decode: q [B][Hq][D] BF16 -> out [B][Hq][D] BF16 (allocated when None)."""
+    sd = _seq(cache, block_table, lens, expected_tags)
+    _need(q, "q", BF16)
+    if q.dim() != 3 or q.shape[0] != block_table.shape[0] or q.shape[2] != cache.head_dim:
+        raise ValueError("q must be [B][Hq][D]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", BF16)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if flags is not None:
+        _need(flags, "flags", U32)
+        if flags.numel() != block_table.shape[0]:
+            raise ValueError("flags must hold B words")
+    cd = cache.desc()
+    Hq = q.shape[1]
+    need = lib().pa_decode_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, num_partitions)
+    if need == ctypes.c_size_t(-1).value:
+        raise PAError(-1, "pa_decode_workspace_bytes")
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    if events is None:
+        rc = lib().pa_decode(ctypes.byref(cd), ctypes.byref(sd), Hq, _ptr(q), _ptr(out),
+                             float(softmax_scale), num_partitions, _ptr(flags), ws_ptr, ws_bytes,
+                             _stream(stream))
+    else:
+        for e in events:
+            if e is not None and not e.cuda_event:
+                e.record()  # torch creates the underlying hipEvent on first record
+        ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        rc = lib().pa_decode_timed(ctypes.byref(cd), ctypes.byref(sd), Hq, _ptr(q), _ptr(out),
+                                   float(softmax_scale), num_partitions, _ptr(flags), ws_ptr,
+                                   ws_bytes, _stream(stream), ev)
+    if rc != 0:
+        raise PAError(rc, "pa_decode")
+    return out
+
+
+def version():
+    return lib().pa_version()

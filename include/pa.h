@@ -1,0 +1,209 @@
+/*
+ * pa.h -- paged decode attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library implements the decode step over a paged KV cache:
+ *   - pa_cache_append writes new K/V tokens into physical pages through a
+ *     block table, quantising to FP8 e4m3 with per-(page, KV head) scales
+ *     when the cache is FP8;
+ *   - pa_decode checks the page tags a request expects, then runs grouped-
+ *     query attention of one query token per sequence over every cached token.
+ *
+ * Sources (web pages; the citations name the page title and the passage):
+ *   [paging]  "How we built the most efficient inference engine for
+ *             Cloudflare's network", section "Batching to feed the Tensor
+ *             Cores": the KV cache is split into pages assigned on demand, and
+ *             each decoded token revisits all cached K/V of its sequence.
+ *   [table]   "Making Workers AI faster and more efficient" (KV cache
+ *             compression page), section "KV cache compression goes open
+ *             source": a block table of integer indices maps a sequence onto
+ *             blocks; a table per head lets heads keep different token counts.
+ *   [fp8]     "Cloudflare quantizes Kimi and GLM caches for 41% faster
+ *             inference", KV cache quantization paragraph: the cache is held
+ *             in FP8 e4m3 instead of BF16, half the bytes, for the
+ *             memory-bound decode phase.
+ *   [tags]    same page, integrity-check paragraph: every physical page has a
+ *             tag that changes on reallocation; the server records the
+ *             (page, tag) pairs each request expects; a separate batch
+ *             validation checks them before decode reads the cache; a request
+ *             that fails is aborted; with checking off the tracker is a no-op.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers unless stated otherwise; the
+ *     descriptors themselves are host structs read during the call.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no state between calls, never synchronises the stream, and is
+ *     reentrant.  Buffers must stay alive until the stream work completes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Argument errors return a negative PA_ERR_* code before anything is
+ *     enqueued.  Data-dependent problems (bad page ids, stale tags, oversize
+ *     lengths) are never returned: they set bits in the device `flags` array.
+ *   - The element type of BF16 tensors is the raw 16-bit pattern (uint16_t).
+ *
+ * Physical cache layout (S = page_size = 16, D = head_dim in {64, 128},
+ * e = bytes per element: 2 for BF16, 1 for FP8):
+ *   SEQ  layout: K and V pools are [num_pages][num_kv_heads][block];
+ *                block table int32 [batch][table_width]; lens int32 [batch].
+ *   HEAD layout: K and V pools are [num_pages][block] (a page belongs to one
+ *                (sequence, KV head) unit); table int32
+ *                [batch][num_kv_heads][table_width]; lens [batch][num_kv_heads].
+ *   A block holds the S x D elements of one (page, head).  Inside it the
+ *   elements are arranged so that each 64-lane load of the decode kernel
+ *   reads 1 KiB contiguously (let CE = 16 / e, elements per 16-byte chunk):
+ *     K(t, d) at element  (d / (4*CE)) * (S * 4*CE) + t * (4*CE) + d % (4*CE)
+ *             (the block is split into 64-byte column segments, each [S][4*CE]);
+ *     V(t, d) with c = d % 16, j = d / 16, TPC = CE / 4 (tiles per chunk):
+ *             at element ((((j / TPC) * 16 + c) * 4 + t / 4) * TPC + j % TPC) * 4 + t % 4
+ *             (V is stored transposed, token-minor, in 16 x 4 MFMA tiles).
+ *   Token t of a unit lives in page table[t / S], slot t % S.
+ *   FP8 scales (float): SEQ [num_pages][num_kv_heads], HEAD [num_pages];
+ *   the value of an element is decode_e4m3(code) * scale[page][head].
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *pa_stream_t; /* identical to hipStream_t */
+typedef struct ihipEvent_t *pa_event_t;   /* identical to hipEvent_t */
+
+enum { PA_LAYOUT_SEQ = 0, PA_LAYOUT_HEAD = 1 };
+enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 /* OCP E4M3 ("fn"): max 448, no inf */ };
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad enum */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, page_size not 16, GQA group > 16 */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_LAUNCH = -4       /* the HIP runtime refused a kernel launch */
+};
+
+/* Bits of the per-sequence flags word ([tags]: a request with any bit set is
+ * to be aborted; its output rows are +0.0 and its pages are not read). */
+enum {
+  PA_FLAG_TAG_MISMATCH = 1u, /* expected tag != page tag for a page it would read */
+  PA_FLAG_PAGE_OOB = 2u,     /* a page id it would read or write is outside [0, num_pages) */
+  PA_FLAG_LEN_OVERFLOW = 4u  /* a length exceeds table_width * page_size */
+};
+
+/* The physical cache ([paging], [table], [fp8], [tags]). */
+typedef struct {
+  int32_t layout;       /* PA_LAYOUT_SEQ or PA_LAYOUT_HEAD */
+  int32_t kv_dtype;     /* PA_KV_BF16 or PA_KV_FP8_E4M3 */
+  int32_t num_pages;    /* P */
+  int32_t page_size;    /* S, must be 16 */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D, 64 or 128 */
+  void *k_pages;        /* K pool, 256-byte aligned, layout above */
+  void *v_pages;        /* V pool, 256-byte aligned, layout above */
+  float *k_scale;       /* FP8 only (else NULL): per (page, head) */
+  float *v_scale;       /* FP8 only (else NULL) */
+  const uint32_t *page_tags; /* [P] current tag of every page; may be NULL when never validated */
+} pa_cache_desc;
+
+/* The logical view of one batch of sequences. */
+typedef struct {
+  int32_t batch;               /* B */
+  int32_t table_width;         /* W, entries per table row */
+  const int32_t *block_table;  /* SEQ [B][W], HEAD [B][Hkv][W]; entries past a unit's
+                                  pages are never read */
+  const int32_t *lens;         /* SEQ [B], HEAD [B][Hkv]: tokens held (decode: tokens attended) */
+  const uint32_t *expected_tags; /* same shape as block_table; NULL = no-op tracker */
+} pa_seq_desc;
+
+/*
+ * Size in bytes of one pool (K or V) for this cache shape: num_pages *
+ * (Hkv for SEQ, 1 for HEAD) * S * D * e.  An FP8 pool is half a BF16 pool
+ * ([fp8]).  Returns 0 for an invalid descriptor.
+ */
+size_t pa_pool_bytes(const pa_cache_desc *cache);
+
+/*
+ * Append tokens ([paging] pages assigned on demand, [fp8] quantisation).
+ *
+ * For every unit u (SEQ: sequence b, all heads; HEAD: (b, h)) writes the
+ * n_new[u] tokens k_new/v_new[b][h][0 .. n_new[u]) at logical positions
+ * seq->lens[u] .. seq->lens[u] + n_new[u] - 1 through the block table.
+ *   n_new:  device int32, SEQ [B], HEAD [B][Hkv]; 0 <= n_new <= n_max.
+ *   k_new, v_new: device BF16 [B][Hkv][n_max][D].
+ *   seq->lens are the lengths BEFORE the append; the library never updates
+ *   lengths or the table.  seq->expected_tags is ignored (tags are checked
+ *   before reads only).
+ * BF16 caches get a copy of the bits.  FP8 caches, per (page, head) and
+ * separately for K and V: s = fl32(amax / 448) over every value written since
+ * the page was last started at slot 0 (a write starting at slot 0 resets the
+ * page), codes = RNE_e4m3(saturate(fl32(x / s))); when the new values raise the
+ * scale, codes already in the page are re-quantised as
+ * RNE_e4m3(saturate(fl32(fl32(decode(c) * s_old) / s_new))).
+ * Tokens whose page id is out of range, or beyond table_width * S, are not
+ * written.  flags (device uint32 [B], may be NULL) is overwritten with
+ * PA_FLAG_PAGE_OOB / PA_FLAG_LEN_OVERFLOW bits of this call.
+ * Pages must not be shared by two units within one call.
+ */
+int pa_cache_append(const pa_cache_desc *cache, const pa_seq_desc *seq, const int32_t *n_new,
+                    int32_t n_max, const uint16_t *k_new, const uint16_t *v_new, uint32_t *flags,
+                    pa_stream_t stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for this shape and partition
+ * count (0 = the library's choice).  0 when the decode needs none (one
+ * partition per unit).  Returns (size_t)-1 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                                 int32_t num_q_heads, int32_t num_partitions);
+
+/* Number of token partitions pa_decode will use for this shape (after the
+ * automatic choice when num_partitions == 0); negative PA_ERR_* on error. */
+int pa_decode_num_partitions(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                             int32_t num_q_heads, int32_t num_partitions);
+
+/*
+ * Decode attention ([paging], [table], [fp8], [tags]).
+ *
+ * q: device BF16 [B][Hq][D], one query token per sequence; out: device BF16
+ * [B][Hq][D].  Query head hq attends with KV head hq / (Hq / Hkv).  For each
+ * unit, all lens[u] tokens are attended with scores softmax_scale * q.k,
+ * softmax over tokens, output sum of weights * V, rounded to BF16 (nearest
+ * even); fp32 accumulation.
+ *
+ * Integrity check: when seq->expected_tags != NULL, a separate validation
+ * kernel runs first and overwrites flags[b] (required, device uint32 [B]) with
+ * the PA_FLAG_* bits of sequence b over the ceil(len / S) entries each unit
+ * reads.  When expected_tags == NULL but flags != NULL, only the page-range
+ * and length bits are computed.  When both are NULL nothing is checked (the
+ * no-op tracker): the caller guarantees valid ids and lengths; the kernels
+ * still never read outside the pool or past table_width.
+ * Rows of flagged sequences and of units with no tokens are written as +0.0.
+ *
+ * num_partitions: split of each unit's tokens (split-K); 0 = automatic.
+ * workspace: device buffer of at least pa_decode_workspace_bytes(...) bytes,
+ * 256-byte aligned (may be NULL when that size is 0).
+ */
+int pa_decode(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+              const uint16_t *q, uint16_t *out, float softmax_scale, int32_t num_partitions,
+              uint32_t *flags, void *workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * pa_decode, plus timing events recorded on `stream` around its kernels:
+ * events[0] before validation, events[1] before attention, events[2] after
+ * attention, events[3] after the partition reduce.  Any entry may be NULL.
+ */
+int pa_decode_timed(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+                    const uint16_t *q, uint16_t *out, float softmax_scale, int32_t num_partitions,
+                    uint32_t *flags, void *workspace, size_t workspace_bytes, pa_stream_t stream,
+                    pa_event_t const events[4]);
+
+/* Static text for a PA_* return code. */
+const char *pa_strerror(int code);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

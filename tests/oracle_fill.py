@@ -52,3 +52,63 @@ def dense_tokens(kv_b, layout, h):
     K = np.concatenate([k_hist[h, :n], k_new[h]], axis=0)
     V = np.concatenate([v_hist[h, :n], v_new[h]], axis=0)
     return K, V
+
+
+def oracle_sequence(w, b):
+    """Oracle result of sequence b alone, on a compact local pool.
+
+    The sequence's pages are renumbered 0..n-1 (the result does not depend on
+    physical page ids: page-permutation invariance is pinned separately).
+    Returns dict(pages=global page ids [n], k, v = local logical pools [n][H][S][D],
+    k_scale, v_scale = [n][H] or None, out = fp64 [Hq][D] (unflagged result)).
+    """
+    from oracle import oracle_decode
+
+    rows = w.block_table[b:b + 1]
+    lens = w.lens[b:b + 1]
+    need = -(-lens.astype(np.int64) // w.S)
+    flat_rows = rows.reshape(-1, w.W)
+    flat_need = need.reshape(-1)
+    pages = np.concatenate([flat_rows[r, :min(int(n), w.W)] for r, n in enumerate(flat_need)])
+    local = np.full(flat_rows.shape, 0x7FFFFFFF, np.int32)
+    k = 0
+    for r, n in enumerate(flat_need):
+        n = int(min(n, w.W))
+        local[r, :n] = np.arange(k, k + n, dtype=np.int32)
+        k += n
+    local = local.reshape(rows.shape)
+    n_pages = max(len(pages), 1)
+    sub = _SubWorkload(w, b, local, n_pages)
+    cache, _ = oracle_fill(sub, seqs=[0])
+    out = oracle_decode(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
+    return dict(pages=pages, k=cache.k[:len(pages)], v=cache.v[:len(pages)],
+                k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
+                v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)], out=out)
+
+
+class _SubWorkload:
+    """Sequence b of a workload seen as a batch of one with a local page table."""
+
+    def __init__(self, w, b, local_table, n_pages):
+        self._w, self._b = w, b
+        self.layout, self.kv_dtype, self.S, self.W = w.layout, w.kv_dtype, w.S, w.W
+        self.Hkv, self.D, self.P, self.B = w.Hkv, w.D, n_pages, 1
+        self.block_table = local_table
+        self.lens = w.lens[b:b + 1]
+
+    def seq_kv(self, _):
+        return self._w.seq_kv(self._b)
+
+
+def oracle_sequences_parallel(w, seqs, workers=None):
+    """oracle_sequence for several sequences in a process pool."""
+    import multiprocessing
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
+    if workers == 1:
+        return {b: oracle_sequence(w, b) for b in seqs}
+    # spawn: a forked child of a process with live OpenMP/torch thread pools can deadlock
+    with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+        return dict(zip(seqs, ex.map(oracle_sequence, [w] * len(seqs), seqs)))

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/pa.h declares, and rejects bad arguments before any launch.
+
+Device pointers here are fake (aligned, never dereferenced): every call below
+must fail its argument checks and return before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_paged_pa_amd import pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000  # 256-byte aligned stand-in for a device pointer
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pa.LIB_PATH), reason="libpa.so not built")
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    L = pa.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+
+
+def _cache(**kw):
+    d = dict(layout=0, kv_dtype=0, num_pages=100, page_size=16, num_kv_heads=8, head_dim=128,
+             k_pages=FAKE, v_pages=FAKE + (1 << 20), k_scale=None, v_scale=None, page_tags=None)
+    d.update(kw)
+    return pa.CacheDesc(**d)
+
+
+def _seq(**kw):
+    d = dict(batch=4, table_width=64, block_table=FAKE, lens=FAKE + 4096, expected_tags=None)
+    d.update(kw)
+    return pa.SeqDesc(**d)
+
+
+def _decode(cache, seq, hq=32, q=FAKE, out=FAKE, scale=0.088, parts=0, flags=None, ws=None,
+            ws_bytes=0):
+    L = pa.lib()
+    return L.pa_decode(ctypes.byref(cache), ctypes.byref(seq), hq, ctypes.c_void_p(q),
+                       ctypes.c_void_p(out), scale, parts,
+                       ctypes.c_void_p(flags) if flags else None,
+                       ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_pool_bytes_and_the_fp8_halving():
+    """FP8 halves the pool ("Cloudflare quantizes Kimi and GLM caches", KV cache
+    quantization paragraph: context held goes from about 686K to 1.37M tokens)."""
+    import json
+
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "page_size_facts.json")))
+    f = facts["fp8_vs_bf16_context_tokens"]
+    ratio = f["fp8_tokens"] / f["bf16_tokens"]
+    L = pa.lib()
+    bf = L.pa_pool_bytes(ctypes.byref(_cache(kv_dtype=0)))
+    f8 = L.pa_pool_bytes(ctypes.byref(_cache(kv_dtype=1)))
+    assert bf == 100 * 8 * 16 * 128 * 2
+    assert abs(bf / f8 - ratio) < 0.01
+    assert L.pa_pool_bytes(ctypes.byref(_cache(layout=1))) == 100 * 16 * 128 * 2
+    assert L.pa_pool_bytes(ctypes.byref(_cache(kv_dtype=7))) == 0
+
+
+def test_no_paging_window_matches_the_four_prompt_figure():
+    """128K tokens of Llama-3.1-8B BF16 KV per prompt: four fit beside the weights
+    on an 80 GB H100 ("How we built the most efficient inference engine",
+    section "Batching to feed the Tensor Cores")."""
+    import json
+
+    f = json.load(open(os.path.join(ROOT, "tests", "golden", "page_size_facts.json")))
+    f = f["no_paging_128k_prompts_h100"]
+    c = _cache(num_pages=f["window_tokens"] // 16, num_kv_heads=f["llama31_8b_kv_heads"],
+               head_dim=f["llama31_8b_head_dim"])
+    per_layer = 2 * pa.lib().pa_pool_bytes(ctypes.byref(c))        # K and V
+    per_prompt = per_layer * f["llama31_8b_layers"]
+    assert per_prompt == 2 ** 34                                   # 16 GiB per 128K prompt
+    assert round((f["h100_hbm_bytes"] - f["weights_bytes"]) / per_prompt) == f["prompts"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=32), -2), (dict(head_dim=96), -2), (dict(layout=5), -1),
+    (dict(kv_dtype=3), -1), (dict(num_pages=0), -1), (dict(k_pages=None), -1),
+    (dict(k_pages=FAKE + 8), -1), (dict(kv_dtype=1), -1),  # FP8 without scales
+])
+def test_decode_rejects_bad_cache(kw, code):
+    assert _decode(_cache(**kw), _seq()) == code
+
+
+def test_decode_rejects_bad_arguments():
+    c, s = _cache(), _seq()
+    assert _decode(c, s, hq=30) == -1                      # Hq not a multiple of Hkv
+    assert _decode(c, s, hq=8 * 17) == -2                  # group of 17 > 16
+    assert _decode(c, s, q=0) == -1
+    assert _decode(c, s, out=FAKE + 2) == -1               # misaligned output
+    assert _decode(c, s, scale=float("nan")) == -1
+    assert _decode(c, s, parts=-1) == -1
+    assert _decode(c, _seq(batch=0)) == -1
+    assert _decode(c, _seq(table_width=0)) == -1
+    assert _decode(c, _seq(lens=None)) == -1
+    # a tag check needs flags and page tags
+    assert _decode(c, _seq(expected_tags=FAKE)) == -1
+    # more than one partition needs a workspace of the advertised size
+    L = pa.lib()
+    need = L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
+    assert need == 4 * 32 * 4 * (128 * 4) + 4 * 32 * 4 * 2 * 4
+    assert _decode(c, s, parts=4) == -3
+    assert _decode(c, s, parts=4, ws=FAKE, ws_bytes=need - 1) == -3
+    assert _decode(c, s, parts=4, ws=FAKE + 16, ws_bytes=need) == -3
+
+
+def test_partition_choice():
+    L = pa.lib()
+    c = _cache()
+    n = lambda s, p: L.pa_decode_num_partitions(ctypes.byref(c), ctypes.byref(s), 64, p)  # noqa: E731
+    assert n(_seq(batch=64, table_width=2048), 8) == 8
+    assert n(_seq(batch=64, table_width=2048), 0) == 8     # auto: 256 pages per workgroup
+    assert n(_seq(batch=4, table_width=32), 0) == 1        # tiny: one partition, no reduce
+    assert n(_seq(batch=4, table_width=32), 3) == 3
+    assert L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(_seq(table_width=32)), 64, 1) == 0
+
+
+def test_append_rejects_bad_arguments():
+    L = pa.lib()
+    c, s = _cache(), _seq()
+    ap = lambda cc, ss, n_new=FAKE, n_max=4, k=FAKE, v=FAKE, fl=None: L.pa_cache_append(  # noqa: E731
+        ctypes.byref(cc), ctypes.byref(ss), ctypes.c_void_p(n_new) if n_new else None, n_max,
+        ctypes.c_void_p(k) if k else None, ctypes.c_void_p(v) if v else None,
+        ctypes.c_void_p(fl) if fl else None, None)
+    assert ap(c, s, n_new=0) == -1
+    assert ap(c, s, n_max=-1) == -1
+    assert ap(c, s, k=0) == -1
+    assert ap(c, s, v=FAKE + 1) == -1
+    assert ap(_cache(head_dim=80), s) == -2
+    assert ap(c, _seq(block_table=None)) == -1
+    assert ap(c, s, n_max=0) == 0        # nothing to do, nothing launched
+
+
+def test_strerror_and_version():
+    L = pa.lib()
+    assert b"workspace" in L.pa_strerror(-3)
+    assert L.pa_strerror(12345) == b"unknown error code"
+    assert pa.version() >= 100
