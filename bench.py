@@ -150,9 +150,11 @@ def main():
     ap.add_argument("--partitions", type=int, default=-1, help="split-K count (-1: 8 for workload 5, else auto)")
     ap.add_argument("--no-check", action="store_true", help="no-op tracker: skip the tag check")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle's timed sample")
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +172,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
     w = make_workload(args.config, stale_frac=0.0)
     parts = args.partitions if args.partitions >= 0 else (8 if args.config == 5 else 0)
     check = not args.no_check
