@@ -29,23 +29,31 @@ def hipcc_flags():
     ]
 
 
-def build(verbose=False):
-    """Compile every source and link libpa.so; raises on failure."""
-    os.makedirs(LIB_DIR, exist_ok=True)
+def build(verbose=False, extra_flags=(), out_path=None, src_dir=None):
+    """Compile every source and link libpa.so; raises on failure.
+
+    extra_flags (e.g. -D tuning knobs), out_path and src_dir serve parameter
+    sweeps and comparisons with other versions of the sources.
+    """
+    out_path = out_path or LIB_PATH
+    src_dir = src_dir or CSRC
+    out_dir = os.path.dirname(out_path)
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
-    obj_dir = os.path.join(LIB_DIR, "obj")
+    obj_dir = os.path.join(out_dir, "obj_" + os.path.basename(out_path).replace(".", "_"))
     os.makedirs(obj_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
         lang = ["-x", "hip"]
-        cmd = [HIPCC] + hipcc_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + hipcc_flags() + list(extra_flags) + lang + [
+            "-c", os.path.join(src_dir, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     _run(cmd, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 def _run(cmd, verbose):

@@ -1,6 +1,6 @@
 // C-ABI entry points of libpa: argument checks, partition choice, workspace
 // sizing and kernel launches.  Declarations and contracts are in pa.h.
-#include "../../include/pa.h"
+#include "pa.h"
 
 #include <hip/hip_runtime.h>
 
@@ -52,27 +52,35 @@ int check_heads(const pa_cache_desc* c, int32_t num_q_heads) {
 size_t elem_bytes(const pa_cache_desc* c) { return c->kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
 
 // Token partitioning of each unit: partitions are runs of chunk_pages pages.
-// Automatic choice: enough workgroups to cover the 256 compute units several
-// times at the table's capacity, with at least 32 pages (8 per wave) and at
-// most 256 pages per workgroup.
+// Automatic choice: about 2048 partitions at the table's capacity (two waves
+// per SIMD on 256 compute units), 32 to 512 pages each.  A wave streams
+// parts_per_wave consecutive partitions of its unit (writing one partial per
+// partition): measured on MI355X, about 2048 long-running waves move the
+// cache faster than 4096 shorter ones, so small partitions are grouped until
+// the grid drops to that size.
+constexpr int64_t kTargetWaves = 2048;
+
 void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req,
-                       int* chunk_pages, int* num_parts) {
+                       int* chunk_pages, int* num_parts, int* parts_per_wave) {
   const int W = s->table_width;
+  const int64_t units = (int64_t)s->batch * c->num_kv_heads;
   int cp;
   if (req > 0) {
     cp = (W + req - 1) / req;
   } else {
-    const int64_t units = (int64_t)s->batch * c->num_kv_heads;
-    const int64_t target = 2048;
-    int64_t x = (units * W + target - 1) / target;
+    int64_t x = (units * W + kTargetWaves - 1) / kTargetWaves;
     if (x < 32) x = 32;
-    if (x > 256) x = 256;
+    if (x > 512) x = 512;
     cp = (int)x;
   }
   if (cp > W) cp = W;
   if (cp < 1) cp = 1;
+  const int parts = (W + cp - 1) / cp;
+  int ppw = 1;
+  while (ppw * 2 <= parts && units * ((parts + 2 * ppw - 1) / (2 * ppw)) >= kTargetWaves) ppw *= 2;
   *chunk_pages = cp;
-  *num_parts = (W + cp - 1) / cp;
+  *num_parts = parts;
+  if (parts_per_wave) *parts_per_wave = ppw;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -96,8 +104,8 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
   if (seq->expected_tags && (!flags || !cache->page_tags)) return PA_ERR_INVALID_ARG;
   if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
-  int chunk_pages, parts;
-  choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts);
+  int chunk_pages, parts, ppw;
+  choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
   const size_t need = workspace_for(cache, seq, num_q_heads, parts);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
@@ -149,6 +157,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.num_pages = cache->num_pages;
   a.chunk_pages = chunk_pages;
   a.num_parts = parts;
+  a.parts_per_wave = ppw;
   a.score_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   if (pa::launch_attention(a, cache->head_dim, fp8, head, stream) != hipSuccess)
     return PA_ERR_LAUNCH;
@@ -216,7 +225,7 @@ PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, const pa_seq
       check_heads(cache, num_q_heads) != PA_OK || num_partitions < 0)
     return (size_t)-1;
   int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts);
+  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
   return workspace_for(cache, seq, num_q_heads, parts);
 }
 
@@ -228,7 +237,7 @@ PA_API int pa_decode_num_partitions(const pa_cache_desc* cache, const pa_seq_des
   if ((rc = check_heads(cache, num_q_heads)) != PA_OK) return rc;
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
   int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts);
+  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
   return parts;
 }
 

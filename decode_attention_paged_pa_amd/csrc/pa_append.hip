@@ -54,10 +54,6 @@ __device__ inline uint32_t e4m3_rne_sat(float v) {
   return sign | mag;
 }
 
-__device__ inline float e4m3_value(uint32_t code) {
-  return __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
-}
-
 __device__ inline float bf16_value(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
 
 // One workgroup per (unit, touched page).  Grid slot j of a unit is its j-th
@@ -95,7 +91,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   if (!FP8) {
     uint16_t* kb = reinterpret_cast<uint16_t*>(a.k_pages) + blk * BLOCK_ELEMS;
-    uint16_t* vb = reinterpret_cast<uint16_t*>(a.v_pages) + blk * BLOCK_ELEMS;
+    uint16_t* vb = reinterpret_cast<uint16_t*>(a.v_pages) +
+                   v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
     for (int e = threadIdx.x; e < cnt * D; e += blockDim.x) {
       const int s = e / D, d = e - s * D;
       kb[k_elem<D, E>(slot0 + s, d)] = ks[e];
@@ -105,7 +102,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 
   uint8_t* kb = a.k_pages + blk * BLOCK_ELEMS;
-  uint8_t* vb = a.v_pages + blk * BLOCK_ELEMS;
+  uint8_t* vb = a.v_pages + v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
   // amax of the new values, K and V separately
   float mk = 0.f, mv = 0.f;
   for (int e = threadIdx.x; e < cnt * D; e += blockDim.x) {
@@ -139,7 +136,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       for (int e = threadIdx.x; e < slot0 * D; e += blockDim.x) {
         const int t = e / D, d = e - t * D;
         const int off = which ? v_elem<D, E>(t, d) : k_elem<D, E>(t, d);
-        const float back = __fmul_rn(e4m3_value(pb[off]), so);
+        const float back = __fmul_rn(e4m3_to_f32(pb[off]), so);
         pb[off] = (uint8_t)e4m3_rne_sat(__fdiv_rn(back, sn));
       }
     }

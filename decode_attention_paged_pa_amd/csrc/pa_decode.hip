@@ -24,6 +24,38 @@ namespace {
 // sums and f16/bf16 MFMA operands hold without loss of range.
 constexpr float kRescaleSlack = 8.0f;
 
+// Tuning knobs (fixed at build time; the defaults are the measured best).
+#ifndef PA_PIPE_DEPTH
+#define PA_PIPE_DEPTH 2        // pages held in registers per wave (loads in flight + current)
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1          // KV loads marked non-temporal (streamed once)
+#endif
+#ifndef PA_ID_GROUP
+#define PA_ID_GROUP 1          // 64-page chunks of page ids a wave holds at once
+#endif
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 4      // occupancy hint for the register allocator (0: none)
+#endif
+constexpr int kPipe = PA_PIPE_DEPTH;
+static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
+
+// BF16 pages hold twice the bytes in the register ring, so that kernel gets
+// one wave per SIMD less than the FP8 one instead of spilling.
+#if PA_WAVES_PER_EU > 0
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)))
+#else
+#define PA_OCCUPANCY
+#endif
+
+__device__ inline u32x4 load16(const uint8_t* p) {
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
 // ------------------------------------------------------------ validation
 // One workgroup per sequence; integrity check of the pages it will read
 // ("Cloudflare quantizes Kimi and GLM caches for 41% faster inference",
@@ -59,30 +91,32 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
 }
 
 // ------------------------------------------------------------- attention
-// Grid: one workgroup per (unit, partition), unit = (sequence, KV head).
-// A partition is a run of chunk_pages pages of the unit; its 4 waves split it
-// into contiguous sub-runs, each keeping its own (max, sum, O) and merging
-// through LDS at the end.
+// One wave owns one work item = (unit, partition), unit = (sequence, KV
+// head), partition = a run of chunk_pages pages of the unit.  The four waves
+// of a workgroup are independent (no LDS, no barrier): each streams its pages
+// through a register ring and writes its own partial (max, sum, O) -- or, with
+// a single partition, the normalised output -- straight from registers.
 template <int D, bool FP8, bool HEAD>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
   constexpr int E = FP8 ? 1 : 2;               // bytes per cached element
   constexpr int BLOCK = kPageSize * D * E;     // bytes of one (page, head) block
   constexpr int NSEG = BLOCK / 1024;           // 16-byte loads per lane per block
   constexpr int NT = D / 16;                   // 16-dim output tiles
   constexpr int NSTEP = D / 32;                // QK MFMA steps over d
 
-  __shared__ float s_o[kWaves][kMaxGroup][D];
-  __shared__ float s_m[kWaves][kMaxGroup];
-  __shared__ float s_l[kWaves][kMaxGroup];
-
   const int Pn = a.num_parts;
-  const int unit = blockIdx.x / Pn;
-  const int part = blockIdx.x - unit * Pn;
+  const int ppw = a.parts_per_wave;
+  const int groups = (Pn + ppw - 1) / ppw;     // waves per unit
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
+  // readfirstlane: the wave index is uniform, and saying so keeps every
+  // per-page index, bound and branch in scalar registers.
+  const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= a.batch * Hkv * groups) return;
+  const int unit = item / groups;
+  const int part0 = (item - unit * groups) * ppw;  // first partition of this wave
   const int b = unit / Hkv;
   const int h = unit - b * Hkv;
   const int row = HEAD ? unit : b;
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;      // MFMA row/column index owned by this lane
   const int q4 = lane >> 4;     // which quarter of the MFMA K dimension
@@ -91,28 +125,23 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   int L = a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int npages = (L + kPageSize - 1) / kPageSize;
-  const int p0 = part * a.chunk_pages;
-  const int p1 = min(p0 + a.chunk_pages, npages);
+  const int p0 = part0 * a.chunk_pages;
+  const int p1 = min(min(part0 + ppw, Pn) * a.chunk_pages, npages);
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
+  const size_t qrow0 = (size_t)b * Hq + h * G;   // first query row of this unit
   if (flagged || p0 >= p1) {
-    if (Pn == 1) {  // no reduce follows: this workgroup owns the output rows
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-        const int g = i / D, d = i - g * D;
-        a.out[((size_t)b * Hq + h * G + g) * D + d] = 0;
-      }
+    if (Pn == 1) {  // no reduce follows: this wave owns the output rows
+      for (int i = lane; i < G * D; i += 64) a.out[qrow0 * D + i] = 0;
     }
     return;
   }
-  const int np = p1 - p0;
-  const int per = (np + kWaves - 1) / kWaves;
-  const int w0 = p0 + wave * per;
-  const int w1 = min(w0 + per, p1);
+  const int n = p1 - p0;
 
   // Q^T as the B operand of S^T = K Q^T: lane (c, q4) holds query g = c and
   // the 8 dims that the K A-operand places in this lane for each step.
   bf16x8 qop[NSTEP];
   {
-    const uint16_t* qrow = a.q + ((size_t)b * Hq + h * G + (c < G ? c : 0)) * D;
+    const uint16_t* qrow = a.q + (qrow0 + (c < G ? c : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       int d0;
@@ -130,167 +159,216 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_acc = 0.f;
 
-  const int32_t* bt = a.block_table + (size_t)row * a.table_width;
+  const int32_t* bt = a.block_table + (size_t)row * a.table_width + p0;
   const size_t page_stride = HEAD ? (size_t)BLOCK : (size_t)Hkv * BLOCK;
-  const size_t head_off = HEAD ? 0 : (size_t)h * BLOCK;
+  const uint8_t* kpool = a.k_pages + (HEAD ? 0 : (size_t)h * BLOCK);
+  // V blocks sit in other slots than their K blocks (v_block_slot): the next
+  // head's slot of the same page, or the neighbouring page's slot.
+  const bool v_rot = !HEAD && Hkv > 1;
+  const uint8_t* vpool = a.v_pages + (HEAD ? 0 : (size_t)(v_rot ? (h + 1) % Hkv : h) * BLOCK);
+  const float* kscale = FP8 ? a.k_scale + (HEAD ? 0 : h) : nullptr;
+  const float* vscale = FP8 ? a.v_scale + (HEAD ? 0 : h) : nullptr;
+  const int scale_stride = HEAD ? 1 : Hkv;
   const int lane_off = (c * 4 + q4) * 16;
-  const uint8_t* kbase = a.k_pages + head_off + lane_off;
-  const uint8_t* vbase = a.v_pages + head_off + lane_off;
 
-  for (int base = w0; base < w1; base += 64) {
-    const int cnt = min(64, w1 - base);
-    int pid_l = lane < cnt ? bt[base + lane] : 0;
-    pid_l = ((unsigned)pid_l < (unsigned)a.num_pages) ? pid_l : 0;
-    float ks_l = 1.f, vs_l = 1.f;
-    if (FP8) {
-      const size_t si = HEAD ? (size_t)pid_l : (size_t)pid_l * Hkv + h;
-      ks_l = a.k_scale[si];
-      vs_l = a.v_scale[si];
+  // Page ids, one lane per page, for up to kIdGroup * 64 pages at a time: a
+  // wave loads its ids once (and again only every 512 pages) so that no wait
+  // for them sits in the page loop.  Ids out of range (only possible with the
+  // tag check off) are read as page 0 so no access leaves the pool.
+  constexpr int kIdGroup = PA_ID_GROUP;
+  int ids[kIdGroup];
+  int ids_base = 0;
+  auto fetch_ids = [&](int first) {
+#pragma unroll
+    for (int j = 0; j < kIdGroup; ++j) {
+      const int k = first + 64 * j + lane;
+      ids[j] = k < n ? bt[k] : 0;
     }
-
-    auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], int k) {
-      const int pid = __builtin_amdgcn_readlane(pid_l, k);
-      const uint8_t* kp = kbase + (size_t)pid * page_stride;
-      const uint8_t* vp = vbase + (size_t)pid * page_stride;
+  };
+  fetch_ids(0);
+  auto page_id = [&](int k) {  // k is wave-uniform, ids_base <= k < ids_base + 512
+    const int r = k - ids_base;
+    int v = ids[0];
 #pragma unroll
-      for (int i = 0; i < NSEG; ++i) {
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + i * 1024));
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 1024));
-      }
-    };
+    for (int j = 1; j < kIdGroup; ++j) v = (r >> 6) == j ? ids[j] : v;
+    const int pid = __builtin_amdgcn_readlane(v, r & 63);
+    return (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+  };
 
-    auto compute = [&](const u32x4 (&kr)[NSEG], const u32x4 (&vr)[NSEG], int k) {
-      const int page = base + k;
-      float kfac = a.score_scale_log2;
-      float vsc = 1.f;
+  // Page k's block: a scalar base address plus this lane's 16-byte chunk, so
+  // that every load is one 1 KiB contiguous wave access.  FP8 scales of the
+  // page are requested with its data.
+  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int k) {
+    const int pid = page_id(k);
+    const uint8_t* kp = kpool + (size_t)pid * page_stride;
+    const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
+    const uint8_t* vp = vpool + (size_t)vpid * page_stride;
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      kr[i] = load16(kp + lane_off + i * 1024);
+      vr[i] = load16(vp + lane_off + i * 1024);
+    }
+    if (FP8) {
+      // A per-lane zero the compiler cannot see through keeps these two loads
+      // on the vector path: they then complete in order with the page data,
+      // whereas scalar loads complete out of order and each wait for one
+      // would wait for all of them.
+      int zero = 0;
+      asm volatile("" : "+v"(zero));
+      ksc = kscale[(size_t)pid * scale_stride + zero];
+      vsc = vscale[(size_t)pid * scale_stride + zero];
+    }
+  };
+
+  auto compute = [&](const u32x4 (&kr)[NSEG], const u32x4 (&vr)[NSEG], float ksc, float vsc,
+                     int k) {
+    const int page = p0 + k;
+    float kfac = a.score_scale_log2;
+    if (FP8) kfac *= ksc;
+    // ---- scores S^T (token rows x query columns)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
       if (FP8) {
-        kfac *= __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ks_l), k));
-        vsc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(vs_l), k));
-      }
-      // ---- scores S^T (token rows x query columns)
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NSEG; ++i) {
-        if (FP8) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
-            u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
-            u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          qop[2 * i + hh], acc, 0, 0, 0);
-          }
-        } else {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]), qop[i],
-                                                        acc, 0, 0, 0);
-        }
-      }
-      // lane (c, q4) now holds the scores of query c for tokens 4*q4 + r
-      const int tok0 = page * kPageSize + q4 * 4;
-      const bool tail = page * kPageSize + kPageSize > L;
-      float sc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = acc[r] * kfac;
-      if (tail) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < L) ? sc[r] : -INFINITY;
-      }
-      float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mloc = col_max(mloc);
-      if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_acc *= alpha;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) o[j] *= alpha;
-        m_run = m_new;
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
-      l_acc += (p[0] + p[1]) + (p[2] + p[3]);
-
-      // ---- O^T += V^T P^T; zero V of tokens past L (poisoned slots)
-      uint32_t vmask32 = 0xFFFFFFFFu;
-      uint64_t vmask64 = ~0ull;
-      if (tail) {
-        const int nv = min(max(L - tok0, 0), 4);
-        vmask32 = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
-        vmask64 = nv >= 4 ? ~0ull : ((1ull << (16 * nv)) - 1ull);
-      }
-      if (FP8) {
-        f16x4 pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(p[r] * vsc);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const uint32_t w = vr[j >> 2][j & 3] & vmask32;
-          o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16x4(w), pb, o[j], 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
+          u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
+          u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        qop[2 * i + hh], acc, 0, 0, 0);
         }
       } else {
-        i16x4 pb;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]), qop[i],
+                                                      acc, 0, 0, 0);
+      }
+    }
+    // lane (c, q4) now holds the scores of query c for tokens 4*q4 + r
+    const int tok0 = page * kPageSize + q4 * 4;
+    const bool tail = page * kPageSize + kPageSize > L;
+    float sc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = __builtin_bit_cast(short, (__bf16)p[r]);
+    for (int r = 0; r < 4; ++r) sc[r] = acc[r] * kfac;
+    if (tail) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < L) ? sc[r] : -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mloc = col_max(mloc);
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_acc *= alpha;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) o[j] *= alpha;
+      m_run = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
+    l_acc += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // ---- O^T += V^T P^T; on the last page zero V of tokens past L (the
+    // slots may hold anything, and 0 * NaN would poison the sum)
+    if (FP8) {
+      f16x4 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(p[r] * vsc);
+      uint32_t vmask = 0xFFFFFFFFu;
+      if (tail) {
+        const int nv = min(max(L - tok0, 0), 4);
+        vmask = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        uint32_t w = vr[j >> 2][j & 3];
+        if (tail) w &= vmask;
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, fp8x4_to_f16x4(w)),
+                                                     pb, o[j], 0, 0, 0);
+      }
+    } else {
+      i16x4 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] = __builtin_bit_cast(short, (__bf16)p[r]);
+      uint64_t vmask = ~0ull;
+      if (tail) {
+        const int nv = min(max(L - tok0, 0), 4);
+        vmask = nv >= 4 ? ~0ull : ((1ull << (16 * nv)) - 1ull);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const u32x4& seg = vr[j >> 1];
+        uint64_t w = ((uint64_t)seg[2 * (j & 1) + 1] << 32) | seg[2 * (j & 1)];
+        if (tail) w &= vmask;
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, w), pb, o[j],
+                                                         0, 0, 0);
+      }
+    }
+  };
+
+  // This wave's result for partition `part`: the normalised output when the
+  // unit has a single partition, else the partial (max, sum, unnormalised O).
+  auto emit = [&](int part) {
+    const float l_tot = col_sum(l_acc);
+    if (c < G) {
+      const size_t qrow = qrow0 + c;
+      if (Pn == 1) {
+        const float inv = 1.f / l_tot;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          const u32x4& seg = vr[j >> 1];
-          uint64_t w = ((uint64_t)seg[2 * (j & 1) + 1] << 32) | seg[2 * (j & 1)];
-          w &= vmask64;
-          o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, w), pb, o[j],
-                                                           0, 0, 0);
+          uint32_t lo = (uint32_t)bf16_rne(o[j][0] * inv) | ((uint32_t)bf16_rne(o[j][1] * inv) << 16);
+          uint32_t hi = (uint32_t)bf16_rne(o[j][2] * inv) | ((uint32_t)bf16_rne(o[j][3] * inv) << 16);
+          *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
+        }
+      } else {
+        float* po = a.part_o + (qrow * Pn + part) * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = o[j];
+        if (q4 == 0) {
+          a.part_ml[(qrow * Pn + part) * 2 + 0] = m_run;
+          a.part_ml[(qrow * Pn + part) * 2 + 1] = l_tot;
         }
       }
-    };
+    }
+  };
 
-    u32x4 kA[NSEG], vA[NSEG], kB[NSEG], vB[NSEG];
-    load(kA, vA, 0);
-    int k = 0;
-    for (; k + 1 < cnt; k += 2) {
-      load(kB, vB, k + 1);
-      compute(kA, vA, k);
-      if (k + 2 < cnt) load(kA, vA, k + 2);
-      compute(kB, vB, k + 1);
-    }
-    if (k < cnt) compute(kA, vA, k);
-  }
-
-  // ---- merge the waves of this workgroup
-  const float l_tot = col_sum(l_acc);
-  if (c < G) {
+  // Register ring of kPipe pages: page k+kPipe-1 is requested before page k
+  // is consumed.  Past the end the last page is requested again (an L2 hit)
+  // so that every iteration issues the same loads.  At each partition
+  // boundary the finished partition is emitted and the state restarts; the
+  // ring keeps streaming across it.
+  u32x4 kr[kPipe][NSEG], vr[kPipe][NSEG];
+  float ks[kPipe], vs[kPipe];
+  int part = part0;
+  int next_boundary = a.chunk_pages;  // page index (relative to p0) of the next partition
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+  for (int u = 0; u < kPipe - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, n - 1));
+  for (int k0 = 0; k0 < n; k0 += kPipe) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[wave][c][16 * j + 4 * q4 + r] = o[j][r];
-    }
-    if (q4 == 0) {
-      s_m[wave][c] = m_run;
-      s_l[wave][c] = l_tot;
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int g = i / D, d = i - g * D;
-    float M = s_m[0][g];
+    for (int u = 0; u < kPipe; ++u) {
+      const int k = k0 + u;
+      const int kn = min(k + kPipe - 1, n - 1);
+      if (kn >= ids_base + 64 * kIdGroup) {  // the look-ahead leaves the loaded ids
+        ids_base += 64 * kIdGroup;
+        fetch_ids(ids_base);
+      }
+      const int slot = (u + kPipe - 1) % kPipe;  // a constant once the loop is unrolled
+      load(kr[slot], vr[slot], ks[slot], vs[slot], kn);
+      if (k < n) {
+        if (k == next_boundary) {
+          emit(part);
+          ++part;
+          next_boundary += a.chunk_pages;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-      lsum += s_l[w][g] * f;
-      osum += s_o[w][g][d] * f;
-    }
-    const size_t qrow = (size_t)b * Hq + h * G + g;
-    if (Pn == 1) {
-      a.out[qrow * D + d] = bf16_rne(osum / lsum);
-    } else {
-      a.part_o[(qrow * Pn + part) * D + d] = osum;
-      if (d == 0) {
-        a.part_ml[(qrow * Pn + part) * 2 + 0] = M;
-        a.part_ml[(qrow * Pn + part) * 2 + 1] = lsum;
+          for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          m_run = -INFINITY;
+          l_acc = 0.f;
+        }
+        compute(kr[u], vr[u], ks[u], vs[u], k);
       }
     }
   }
+  emit(part);
 }
 
 // ---------------------------------------------------------------- reduce
@@ -331,7 +409,9 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
 
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)a.batch * a.num_kv_heads * a.num_parts;
+  const unsigned groups = (unsigned)(a.num_parts + a.parts_per_wave - 1) / a.parts_per_wave;
+  const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
+  const unsigned grid = (items + kWaves - 1) / kWaves;
   hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD>), dim3(grid), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }

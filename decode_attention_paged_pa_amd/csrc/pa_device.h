@@ -23,10 +23,33 @@ __device__ inline uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Four e4m3 codes (one dword, byte i = element i) -> four BF16 values packed in
-// two dwords.  The hardware conversion to fp32 is exact for OCP e4m3 on gfx950,
-// and every e4m3 value fits in BF16's 8-bit significand, so keeping the upper
-// half of each fp32 is exact as well.
+// Four e4m3 codes (one dword, byte i = element i) -> four BF16 / f16 values
+// packed in two dwords; every e4m3 value is exactly representable in both.
+#ifndef PA_SCALED_CVT
+#define PA_SCALED_CVT 0
+#endif
+#if PA_SCALED_CVT
+// gfx950's scaled pair conversions decode two codes per instruction; with a
+// scale of 1.0 they are exact (checked against the OCP definition for all 256
+// codes).  The packed result is only ever used as a whole dword: extracting
+// single halves from these builtins' results has produced wrong code.
+__device__ inline u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return r;
+}
+
+__device__ inline u32x2 fp8x4_to_f16x4(uint32_t w) {
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  return r;
+}
+#else
+// The conversion to fp32 is exact for OCP e4m3 on gfx950 (checked for all 256
+// codes); keeping the upper half of each fp32 is then an exact BF16, and the
+// round-toward-zero pack to f16 is exact too.
 __device__ inline u32x2 fp8x4_to_bf16x4(uint32_t w) {
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
@@ -36,19 +59,19 @@ __device__ inline u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-// Four e4m3 codes -> four f16 values (exact: e4m3's range and precision are
-// inside f16's, subnormals included).
-__device__ inline f16x4 fp8x4_to_f16x4(uint32_t w) {
+__device__ inline u32x2 fp8x4_to_f16x4(uint32_t w) {
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  auto a = __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y);
-  auto b = __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y);
-  f16x4 r;
-  r[0] = (_Float16)a[0];
-  r[1] = (_Float16)a[1];
-  r[2] = (_Float16)b[0];
-  r[3] = (_Float16)b[1];
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y));
   return r;
+}
+#endif
+
+// Exact decode of one e4m3 code (byte 0 of `code`) to fp32.
+__device__ inline float e4m3_to_f32(uint32_t code) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
 }
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} (one MFMA column).

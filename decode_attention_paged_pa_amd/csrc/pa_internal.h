@@ -7,7 +7,7 @@
 namespace pa {
 
 constexpr int kPageSize = 16;      // tokens per page (S)
-constexpr int kWaves = 4;          // waves per attention workgroup
+constexpr int kWaves = 4;          // waves (independent work items) per attention workgroup
 constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
 
 // Arguments of the attention (partial) kernel.
@@ -25,6 +25,7 @@ struct AttnArgs {
   float* part_ml;            // [B][Hq][Pn][2] running max (log2 domain) and sum
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int chunk_pages, num_parts;
+  int parts_per_wave;        // consecutive partitions of one unit a wave streams through
   float score_scale_log2;    // softmax_scale * log2(e)
 };
 
@@ -53,6 +54,23 @@ struct AppendArgs {
   int pages_per_unit;         // ceil(n_max / S) + 1: grid slots per unit
   bool head_layout, fp8;
 };
+
+// Pool slot of the V block of (page pid, KV head h).  The V block of a
+// (page, head) is not stored at the same slot as its K block: K and V pools
+// are separate allocations, commonly aligned alike, and a wave requests the K
+// and V blocks of a page back to back; at equal offsets both requests fall in
+// the same HBM bank (measured: about 5% of decode bandwidth lost).  SEQ layout
+// with several heads: head h's V goes to head (h + 1) % Hkv's slot of the same
+// page; otherwise page pid's V goes to page pid ^ 1's slot (pid itself when
+// pid ^ 1 is past the pool).  A bijection, so every slot is still used once.
+__host__ __device__ inline size_t v_block_slot(int pid, int h, int num_kv_heads, int num_pages,
+                                               bool head_layout) {
+  if (!head_layout && num_kv_heads > 1)
+    return (size_t)pid * num_kv_heads + (h + 1 == num_kv_heads ? 0 : h + 1);
+  const int q = pid ^ 1;
+  const int p = q < num_pages ? q : pid;
+  return head_layout ? (size_t)p : (size_t)p * num_kv_heads + h;
+}
 
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,

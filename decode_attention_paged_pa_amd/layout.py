@@ -8,6 +8,8 @@ e = bytes per element, CE = 16 / e elements per 16-byte chunk.
   K(t, d) at (d // (4 CE)) * (S * 4 CE) + t * 4 CE + d % (4 CE)
   V(t, d) at ((((j // TPC) * 16 + c) * 4 + t // 4) * TPC + j % TPC) * 4 + t % 4
           with c = d % 16, j = d // 16, TPC = CE // 4
+The V block of a logical (page, head) is stored in another pool slot than its
+K block (v_block_slots).
 """
 import numpy as np
 
@@ -29,11 +31,29 @@ def v_offsets(D, esize):
     return ((((j // tpc) * 16 + c) * 4 + t // 4) * tpc + j % tpc) * 4 + t % 4
 
 
+def v_block_slots(layout, num_pages, num_kv_heads):
+    """Pool slot (page, head) holding the V block of each logical (page, head).
+
+    SEQ with several heads: head h's V block is in head (h + 1) % Hkv's slot of
+    the same page; otherwise page p's V block is in page p ^ 1's slot (p itself
+    when p ^ 1 is past the pool).  Returns (page index [P][H], head index [P][H]).
+    """
+    H = num_kv_heads if layout == "seq" else 1
+    p = np.repeat(np.arange(num_pages)[:, None], H, axis=1)
+    h = np.repeat(np.arange(H)[None, :], num_pages, axis=0)
+    if layout == "seq" and num_kv_heads > 1:
+        return p, (h + 1) % num_kv_heads
+    q = p ^ 1
+    return np.where(q < num_pages, q, p), h
+
+
 def pool_to_logical(pool_bytes, which, layout, kv_dtype, num_pages, num_kv_heads, head_dim):
     """Raw pool bytes (numpy uint8, flat) -> [P][H][S][D] (H = Hkv, or 1 for HEAD)."""
     esize = 1 if kv_dtype == "fp8" else 2
     dt = np.uint8 if esize == 1 else np.uint16
     H = num_kv_heads if layout == "seq" else 1
     blocks = np.asarray(pool_bytes).view(dt).reshape(num_pages, H, S * head_dim)
-    off = k_offsets(head_dim, esize) if which == "k" else v_offsets(head_dim, esize)
-    return blocks[:, :, off]
+    if which == "k":
+        return blocks[:, :, k_offsets(head_dim, esize)]
+    sp, sh = v_block_slots(layout, num_pages, num_kv_heads)
+    return blocks[sp, sh][:, :, v_offsets(head_dim, esize)]

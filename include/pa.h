@@ -54,6 +54,12 @@
  *     V(t, d) with c = d % 16, j = d / 16, TPC = CE / 4 (tiles per chunk):
  *             at element ((((j / TPC) * 16 + c) * 4 + t / 4) * TPC + j % TPC) * 4 + t % 4
  *             (V is stored transposed, token-minor, in 16 x 4 MFMA tiles).
+ *   The V block of logical (page p, head h) is stored in another pool slot
+ *   than its K block, so that the two requests a decode wave makes for one
+ *   page never meet at equal offsets of two alike-aligned pools (which costs
+ *   HBM bank conflicts): SEQ with Hkv > 1 stores it in head (h + 1) % Hkv's
+ *   slot of page p; otherwise in page (p ^ 1)'s slot, or p's own when p ^ 1
+ *   is not below num_pages.
  *   Token t of a unit lives in page table[t / S], slot t % S.
  *   FP8 scales (float): SEQ [num_pages][num_kv_heads], HEAD [num_pages];
  *   the value of an element is decode_e4m3(code) * scale[page][head].

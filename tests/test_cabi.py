@@ -127,7 +127,7 @@ def test_partition_choice():
     c = _cache()
     n = lambda s, p: L.pa_decode_num_partitions(ctypes.byref(c), ctypes.byref(s), 64, p)  # noqa: E731
     assert n(_seq(batch=64, table_width=2048), 8) == 8
-    assert n(_seq(batch=64, table_width=2048), 0) == 8     # auto: 256 pages per workgroup
+    assert n(_seq(batch=64, table_width=2048), 0) == 4     # auto: 512 pages per partition
     assert n(_seq(batch=4, table_width=32), 0) == 1        # tiny: one partition, no reduce
     assert n(_seq(batch=4, table_width=32), 3) == 3
     assert L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(_seq(table_width=32)), 64, 1) == 0
