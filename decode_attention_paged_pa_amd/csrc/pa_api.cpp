@@ -76,8 +76,8 @@ void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req
   if (cp > W) cp = W;
   if (cp < 1) cp = 1;
   const int parts = (W + cp - 1) / cp;
-  int ppw = 1;
-  while (ppw * 2 <= parts && units * ((parts + 2 * ppw - 1) / (2 * ppw)) >= kTargetWaves) ppw *= 2;
+  int ppw = 1;  // at most 2: the attention kernel parks one finished partition per wave
+  if (parts >= 2 && units * ((parts + 1) / 2) >= kTargetWaves) ppw = 2;
   *chunk_pages = cp;
   *num_parts = parts;
   if (parts_per_wave) *parts_per_wave = ppw;
@@ -158,6 +158,12 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.chunk_pages = chunk_pages;
   a.num_parts = parts;
   a.parts_per_wave = ppw;
+  // XCD-aware workgroup order needs whole groups of 4 heads; the SEQ layout
+  // gains most from it (the heads of a page share its blocks and scales).
+  a.xcd_order = (cache->num_kv_heads % pa::kWaves == 0) ? 1 : 0;
+#ifdef PA_NO_XCD_ORDER
+  a.xcd_order = 0;
+#endif
   a.score_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   if (pa::launch_attention(a, cache->head_dim, fp8, head, stream) != hipSuccess)
     return PA_ERR_LAUNCH;

@@ -31,8 +31,8 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1          // KV loads marked non-temporal (streamed once)
 #endif
-#ifndef PA_ID_GROUP
-#define PA_ID_GROUP 1          // 64-page chunks of page ids a wave holds at once
+#ifndef PA_THROTTLE
+#define PA_THROTTLE 1          // each wave waits for its loads before requesting the next page
 #endif
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 4      // occupancy hint for the register allocator (0: none)
@@ -103,6 +103,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   constexpr int NSEG = BLOCK / 1024;           // 16-byte loads per lane per block
   constexpr int NT = D / 16;                   // 16-dim output tiles
   constexpr int NSTEP = D / 32;                // QK MFMA steps over d
+  // A wave streams at most two partitions; the state of the first is parked
+  // here (O, max, per-lane sum; one column per lane) until the wave ends.
+  constexpr int kStash = 4 * NT + 2;
+  __shared__ float s_stash[kWaves][kStash][64];
 
   const int Pn = a.num_parts;
   const int ppw = a.parts_per_wave;
@@ -110,12 +114,35 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   // readfirstlane: the wave index is uniform, and saying so keeps every
   // per-page index, bound and branch in scalar registers.
-  const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (item >= a.batch * Hkv * groups) return;
-  const int unit = item / groups;
-  const int part0 = (item - unit * groups) * ppw;  // first partition of this wave
-  const int b = unit / Hkv;
-  const int h = unit - b * Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b, h, g;  // sequence, KV head, partition group of this wave
+  if (a.xcd_order) {
+    // Workgroups are dealt to the 8 XCDs in turn (id % 8).  A workgroup holds
+    // 4 heads of one (sequence, partition group) pair, and the Hkv/4
+    // workgroups of a pair get ids 8 apart -- same XCD, launched together --
+    // so all heads of a page meet in one L2 (its scales, its table entries,
+    // and the neighbouring head blocks of the SEQ layout).  Pairs are
+    // numbered partition-major, so an XCD's share is spread over sequences
+    // rather than tied to one partition index (late partitions of short
+    // sequences are empty).
+    const int hgs = Hkv / kWaves;               // head groups per pair
+    const int x = blockIdx.x;
+    const int pair = (x / (8 * hgs)) * 8 + (x % 8);
+    const int hg = (x / 8) % hgs;
+    if (pair >= a.batch * groups) return;
+    g = pair / a.batch;
+    b = pair - g * a.batch;
+    h = hg * kWaves + wave;
+  } else {
+    const int item = blockIdx.x * kWaves + wave;
+    if (item >= a.batch * Hkv * groups) return;
+    const int unit = item / groups;
+    g = item - unit * groups;
+    b = unit / Hkv;
+    h = unit - b * Hkv;
+  }
+  const int unit = b * Hkv + h;
+  const int part0 = g * ppw;  // first partition of this wave
   const int row = HEAD ? unit : b;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;      // MFMA row/column index owned by this lane
@@ -171,35 +198,33 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int scale_stride = HEAD ? 1 : Hkv;
   const int lane_off = (c * 4 + q4) * 16;
 
-  // Page ids, one lane per page, for up to kIdGroup * 64 pages at a time: a
-  // wave loads its ids once (and again only every 512 pages) so that no wait
-  // for them sits in the page loop.  Ids out of range (only possible with the
-  // tag check off) are read as page 0 so no access leaves the pool.
-  constexpr int kIdGroup = PA_ID_GROUP;
-  int ids[kIdGroup];
-  int ids_base = 0;
-  auto fetch_ids = [&](int first) {
+  // Page ids, one lane per page, 512 pages (8 registers) at a time.  They are
+  // loaded, and waited for, before the page loop of each 512-page segment:
+  // a load inside the loop would put a join in front of every use, and the
+  // compiler then waits for all outstanding loads there on every page.  The
+  // look-ahead page's id is always read from ids[0]; the registers shift down
+  // by one when the look-ahead enters the next 64 pages (constant indices
+  // only, so the array stays in registers).  Ids out of range (only possible
+  // with the tag check off) are read as page 0 so no access leaves the pool.
+  constexpr int kIdRegs = 8;
+  constexpr int kSegPages = 64 * kIdRegs;
+  int ids[kIdRegs];
+  int id_chunk = 0;      // the 64-page chunk of the segment that ids[0] holds
+  auto page_id = [&](int r) {  // r: page index within the segment, uniform, non-decreasing
+    if ((r >> 6) != id_chunk) {
 #pragma unroll
-    for (int j = 0; j < kIdGroup; ++j) {
-      const int k = first + 64 * j + lane;
-      ids[j] = k < n ? bt[k] : 0;
+      for (int t = 0; t + 1 < kIdRegs; ++t) ids[t] = ids[t + 1];
+      ++id_chunk;
     }
-  };
-  fetch_ids(0);
-  auto page_id = [&](int k) {  // k is wave-uniform, ids_base <= k < ids_base + 512
-    const int r = k - ids_base;
-    int v = ids[0];
-#pragma unroll
-    for (int j = 1; j < kIdGroup; ++j) v = (r >> 6) == j ? ids[j] : v;
-    const int pid = __builtin_amdgcn_readlane(v, r & 63);
+    const int pid = __builtin_amdgcn_readlane(ids[0], r & 63);
     return (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
   };
 
   // Page k's block: a scalar base address plus this lane's 16-byte chunk, so
   // that every load is one 1 KiB contiguous wave access.  FP8 scales of the
   // page are requested with its data.
-  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int k) {
-    const int pid = page_id(k);
+  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int r) {
+    const int pid = page_id(r);
     const uint8_t* kp = kpool + (size_t)pid * page_stride;
     const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
     const uint8_t* vp = vpool + (size_t)vpid * page_stride;
@@ -332,43 +357,76 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  // Register ring of kPipe pages: page k+kPipe-1 is requested before page k
-  // is consumed.  Past the end the last page is requested again (an L2 hit)
-  // so that every iteration issues the same loads.  At each partition
-  // boundary the finished partition is emitted and the state restarts; the
-  // ring keeps streaming across it.
+  // Register ring of kPipe pages: page r+kPipe-1 is requested before page r
+  // is consumed.  Past the end of a segment the last page is requested again
+  // (an L2 hit) so that every iteration issues the same loads.  At each
+  // partition boundary the finished partition is emitted and the state
+  // restarts; the ring keeps streaming across it.
   u32x4 kr[kPipe][NSEG], vr[kPipe][NSEG];
   float ks[kPipe], vs[kPipe];
   int part = part0;
   int next_boundary = a.chunk_pages;  // page index (relative to p0) of the next partition
+  float (*stash)[64] = s_stash[wave];
+  for (int seg = 0; seg < n; seg += kSegPages) {
+    const int m = min(kSegPages, n - seg);
 #pragma unroll
-  for (int u = 0; u < kPipe - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, n - 1));
-  for (int k0 = 0; k0 < n; k0 += kPipe) {
+    for (int j = 0; j < kIdRegs; ++j) {
+      const int k = seg + 64 * j + lane;
+      ids[j] = k < n ? bt[k] : 0;
+    }
+    // wait for the ids here, once per segment (see above)
+    int last = __builtin_amdgcn_readfirstlane(ids[kIdRegs - 1]);
+    asm volatile("" : : "s"(last));
+    id_chunk = 0;
 #pragma unroll
-    for (int u = 0; u < kPipe; ++u) {
-      const int k = k0 + u;
-      const int kn = min(k + kPipe - 1, n - 1);
-      if (kn >= ids_base + 64 * kIdGroup) {  // the look-ahead leaves the loaded ids
-        ids_base += 64 * kIdGroup;
-        fetch_ids(ids_base);
-      }
-      const int slot = (u + kPipe - 1) % kPipe;  // a constant once the loop is unrolled
-      load(kr[slot], vr[slot], ks[slot], vs[slot], kn);
-      if (k < n) {
-        if (k == next_boundary) {
-          emit(part);
-          ++part;
-          next_boundary += a.chunk_pages;
+    for (int u = 0; u < kPipe - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1));
+    for (int r0 = 0; r0 < m; r0 += kPipe) {
 #pragma unroll
-          for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          m_run = -INFINITY;
-          l_acc = 0.f;
+      for (int u = 0; u < kPipe; ++u) {
+        const int r = r0 + u;                      // page within the segment
+        const int slot = (u + kPipe - 1) % kPipe;  // a constant once the loop is unrolled
+#if PA_THROTTLE
+        // At most one page in flight per wave besides the one being consumed:
+        // measured on MI355X, 2048 waves each keeping two or more pages of
+        // random 2 KiB blocks outstanding move the cache 2-4% slower.
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // s_waitcnt vmcnt(0)
+#endif
+        load(kr[slot], vr[slot], ks[slot], vs[slot], min(r + kPipe - 1, m - 1));
+        if (r < m) {
+          const int k = seg + r;                   // page within this wave's run
+          if (k == next_boundary) {
+            // Park the finished partition in LDS: a global store now would
+            // be waited for by the next page's throttle, and under the full
+            // read stream stores take long to complete (measured: 6% of the
+            // kernel time on the 32K-token FP8 workload).
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[j][r];
+            stash[4 * NT][lane] = m_run;
+            stash[4 * NT + 1][lane] = l_acc;
+            ++part;
+            next_boundary += a.chunk_pages;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run = -INFINITY;
+            l_acc = 0.f;
+          }
+          compute(kr[u], vr[u], ks[u], vs[u], k);
         }
-        compute(kr[u], vr[u], ks[u], vs[u], k);
       }
     }
   }
   emit(part);
+  if (part > part0) {  // the parked first partition
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[j][r] = stash[4 * j + r][lane];
+    m_run = stash[4 * NT][lane];
+    l_acc = stash[4 * NT + 1][lane];
+    emit(part0);
+  }
 }
 
 // ---------------------------------------------------------------- reduce
@@ -410,8 +468,14 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   const unsigned groups = (unsigned)(a.num_parts + a.parts_per_wave - 1) / a.parts_per_wave;
-  const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
-  const unsigned grid = (items + kWaves - 1) / kWaves;
+  unsigned grid;
+  if (a.xcd_order) {  // see attention_kernel: (Hkv / 4) workgroups per pair, in blocks of 8 pairs
+    const unsigned pairs = (unsigned)a.batch * groups;
+    grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
+  } else {
+    const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
+    grid = (items + kWaves - 1) / kWaves;
+  }
   hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD>), dim3(grid), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }

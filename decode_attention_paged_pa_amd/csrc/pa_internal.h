@@ -26,6 +26,7 @@ struct AttnArgs {
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int chunk_pages, num_parts;
   int parts_per_wave;        // consecutive partitions of one unit a wave streams through
+  int xcd_order;             // workgroup order that keeps a page's heads on one XCD
   float score_scale_log2;    // softmax_scale * log2(e)
 };
 

@@ -122,7 +122,7 @@ def test_workload2_reduced_ragged_and_partition_counts():
 
 
 def test_workload2_full():
-    run_case(make_workload(2), partitions=(0, 8, 32))   # 32: a wave streams 4 partitions
+    run_case(make_workload(2), partitions=(0, 8, 32))   # 32: a wave streams 2 partitions
 
 
 def test_workload3_reduced_stale_tags():
@@ -133,7 +133,7 @@ def test_workload3_reduced_stale_tags():
 
 def test_workload3_full_stale_then_valid():
     w = make_workload(3)
-    dw, ora, outs = run_case(w, partitions=(0, 16))       # 16: a wave streams 4 partitions
+    dw, ora, outs = run_case(w, partitions=(0, 16))       # 16: a wave streams 2 partitions
     fl = flags_of(dw)
     assert np.count_nonzero(fl) > 0
     # the same cache with every expected tag valid: all rows compared
