@@ -76,12 +76,27 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
     const int n = (L + kPageSize - 1) / kPageSize;
     const int32_t* bt = a.block_table + (size_t)row * a.table_width;
     const uint32_t* ex = a.expected_tags ? a.expected_tags + (size_t)row * a.table_width : nullptr;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const int pid = bt[i];
-      if ((unsigned)pid >= (unsigned)a.num_pages) {
-        bits |= 2u;
-      } else if (ex && ex[i] != a.page_tags[pid]) {
-        bits |= 1u;
+    // 8 entries per thread per pass, all loads of a pass issued before any
+    // is used: two dependent round trips per pass instead of two per entry.
+    constexpr int kPer = 8;
+    for (int base = 0; base < n; base += kPer * blockDim.x) {
+      int pid[kPer];
+      uint32_t want[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = base + j * blockDim.x + threadIdx.x;
+        pid[j] = i < n ? bt[i] : 0;
+        want[j] = (i < n && ex) ? ex[i] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = base + j * blockDim.x + threadIdx.x;
+        if (i >= n) continue;
+        if ((unsigned)pid[j] >= (unsigned)a.num_pages) {
+          bits |= 2u;
+        } else if (ex && want[j] != a.page_tags[pid[j]]) {
+          bits |= 1u;
+        }
       }
     }
   }
@@ -454,13 +469,32 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   const int Pn = a.num_parts;
   const float* ml = a.part_ml + (size_t)qrow * Pn * 2;
   const float* po = a.part_o + (size_t)qrow * Pn * D + d;
-  float M = ml[0];
-  for (int p = 1; p < nvp; ++p) M = fmaxf(M, ml[2 * p]);
-  float lsum = 0.f, osum = 0.f;
-  for (int p = 0; p < nvp; ++p) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    lsum += ml[2 * p + 1] * f;
-    osum += po[(size_t)p * D] * f;
+  // Partitions in groups of 8, every load of a group issued before use; a
+  // running (max, sum, O) merges the groups in partition order.
+  constexpr int kGrp = 8;
+  float M = -INFINITY, lsum = 0.f, osum = 0.f;
+  for (int p0 = 0; p0 < nvp; p0 += kGrp) {
+    float m[kGrp], l[kGrp], o[kGrp];
+#pragma unroll
+    for (int j = 0; j < kGrp; ++j) {
+      const bool ok = p0 + j < nvp;
+      m[j] = ok ? ml[2 * (p0 + j)] : -INFINITY;
+      l[j] = ok ? ml[2 * (p0 + j) + 1] : 0.f;
+      o[j] = ok ? po[(size_t)(p0 + j) * D] : 0.f;
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < kGrp; ++j) Mg = fmaxf(Mg, m[j]);
+    const float r = __builtin_amdgcn_exp2f(M - Mg);  // M = -inf on the first group: r = 0
+    lsum *= r;
+    osum *= r;
+#pragma unroll
+    for (int j = 0; j < kGrp; ++j) {
+      const float f = __builtin_amdgcn_exp2f(m[j] - Mg);  // empty slots: exp2(-inf) = 0
+      lsum += l[j] * f;
+      osum += o[j] * f;
+    }
+    M = Mg;
   }
   a.out[(size_t)qrow * D + d] = bf16_rne(osum / lsum);
 }

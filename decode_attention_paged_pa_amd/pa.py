@@ -265,3 +265,43 @@ def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags
 
 def version():
     return lib().pa_version()
+
+
+class DecodeStepGraph:
+    """One decode step (append, then decode) captured as a HIP graph and replayed.
+
+    The Infire page ("How we built the most efficient inference engine for
+    Cloudflare's network", section "Rust-precise CUDA kernels") keeps one graph
+    per batch size so back-to-back kernels launch as one construct.  The library
+    allocates nothing and issues no memsets, so its launches capture as they
+    are; every buffer (cache, tables, lengths, q, out, flags, workspace) is
+    fixed at capture time and read again at each replay, so the caller updates
+    their contents in place between replays (new tokens, lengths, tables).
+    """
+
+    def __init__(self, cache, block_table, lens_old, n_new, k_new, v_new, q, lens,
+                 softmax_scale, expected_tags=None, flags=None, num_partitions=0, warmup=1):
+        self.args = (cache, block_table, lens_old, n_new, k_new, v_new, q, lens, softmax_scale,
+                     expected_tags, flags, num_partitions)
+        self.out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        need = workspace_bytes(cache, block_table, lens, q.shape[1], num_partitions)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):       # warm up off the capture, as torch requires
+            for _ in range(warmup):
+                self._step()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._step()
+
+    def _step(self):
+        (cache, bt, lens_old, n_new, k_new, v_new, q, lens, scale, exp, flags, parts) = self.args
+        append(cache, bt, lens_old, n_new, k_new, v_new)
+        decode(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
+               out=self.out, workspace=self.workspace)
+
+    def replay(self):
+        self.graph.replay()
+        return self.out
