@@ -1,9 +1,9 @@
 """Put a synthetic workload on the GPU and fill its paged cache through the library.
 
 The cache is filled the way a decode loop fills it: one bulk pa_cache_append of
-each sequence's first L-1 tokens into empty pages, then the decode step's own
-append of one new token per unit (lengths L-1 -> L), after which decode attends
-L tokens.  Draws come from workloads.Workload (numpy, per-sequence child
+each sequence's first L-T tokens into empty pages, then the decode step's own
+append of its T new tokens per unit (lengths L-T -> L; T = 1 for plain decode,
+the draft count for a multi-query step), after which decode attends L tokens.  Draws come from workloads.Workload (numpy, per-sequence child
 streams), generated on host threads ahead of the uploads.
 """
 from concurrent.futures import ThreadPoolExecutor
@@ -22,8 +22,8 @@ class DeviceWorkload:
     block_table: torch.Tensor
     lens: torch.Tensor          # tokens attended (after the step's append)
     lens_old: torch.Tensor      # lengths before the step's append
-    n_step: torch.Tensor        # ones: tokens appended by the step
-    k_step: torch.Tensor        # [B][Hkv][1][D] bf16: the step's new tokens
+    n_step: torch.Tensor        # tokens appended by the step (T, 0 for empty units)
+    k_step: torch.Tensor        # [B][Hkv][T][D] bf16: the step's new tokens
     v_step: torch.Tensor
     q: torch.Tensor             # [B][Hq][D] bf16
     page_tags: torch.Tensor
@@ -52,14 +52,15 @@ def build_device_workload(w, device="cuda", threads=8, seqs=None, log=None):
     """Upload workload `w` and fill its cache; `seqs` limits the bulk fill (tests)."""
     bt = _dev(w.block_table, device)
     lens = _dev(w.lens, device)
-    lens_old = _dev(np.maximum(w.lens.astype(np.int32) - 1, 0).astype(np.int32), device)
-    n_step = (lens > 0).to(torch.int32)
+    T = w.q_len
+    lens_old = _dev(np.maximum(w.lens.astype(np.int32) - T, 0).astype(np.int32), device)
+    n_step = (lens > 0).to(torch.int32) * T
     page_tags = _dev(w.page_tags, device, torch.int32)
     exp = _dev(w.expected_tags, device, torch.int32)
     q = _dev(w.q, device, torch.bfloat16)
     cache = pa.PagedKVCache(w.layout, w.kv_dtype, w.P, w.Hkv, w.D, device=device,
                             page_tags=page_tags)
-    k_step = np.zeros((w.B, w.Hkv, 1, w.D), np.uint16)
+    k_step = np.zeros((w.B, w.Hkv, T, w.D), np.uint16)
     v_step = np.zeros_like(k_step)
     seqs = list(range(w.B)) if seqs is None else list(seqs)
     zero1 = torch.zeros((1,) + tuple(w.lens.shape[1:]), dtype=torch.int32, device=device)

@@ -31,6 +31,11 @@ so that any one sequence can be regenerated on its own: per KV head h, K
 history [L-1][D], V history, then the new token's K and V (SEQ layout draws
 all heads at once in that order).  All values are N(0, 1) fp32 rounded to BF16.
 A decode step appends the new token, then attends all L tokens.
+
+Multi-query workloads (q_len T > 1, speculative verification) draw the same
+way with T in place of the single new token: per KV head a history of L - T
+tokens, then the T draft tokens; queries are [B][T][Hq][D], drawn in step 4
+instead of the [B][Hq][D] ones.  With T = 1 every draw is the one above.
 """
 from dataclasses import dataclass, field
 
@@ -59,8 +64,9 @@ class Workload:
     page_tags: np.ndarray       # uint32 [P]
     expected_tags: np.ndarray   # uint32, shape of block_table
     stale: np.ndarray           # bool, shape of block_table
-    q: np.ndarray               # uint16 bf16 bits [B][Hq][D]
+    q: np.ndarray               # uint16 bf16 bits [B][Hq][D], or [B][T][Hq][D] when q_len > 1
     seed: int = 0
+    q_len: int = 1              # T: query (draft) tokens per sequence, the last T of each unit
     extra: dict = field(default_factory=dict)
 
     @property
@@ -74,30 +80,31 @@ class Workload:
         """K/V draws of sequence b (bf16 bits).
 
         Returns (k_hist, v_hist, k_new, v_new, n_hist) with k_hist/v_hist
-        [Hkv][max_h(L-1)][D] (rows past a head's own L-1 are zero padding),
-        k_new/v_new [Hkv][1][D] and n_hist int32 [Hkv] = L(b, h) - 1.
+        [Hkv][max_h(L-T)][D] (rows past a head's own L-T are zero padding),
+        k_new/v_new [Hkv][T][D] and n_hist int32 [Hkv] = L(b, h) - T.
         """
         rng = np.random.default_rng(np.random.SeedSequence(self.seed).spawn(self.B)[b])
+        T = self.q_len
         if self.layout == "seq":
             L = int(self.lens[b])
-            n_hist = np.full(self.Hkv, max(L - 1, 0), np.int32)
-            kh = rng.standard_normal((self.Hkv, max(L - 1, 0), self.D), dtype=np.float32)
-            vh = rng.standard_normal((self.Hkv, max(L - 1, 0), self.D), dtype=np.float32)
-            kn = rng.standard_normal((self.Hkv, 1, self.D), dtype=np.float32)
-            vn = rng.standard_normal((self.Hkv, 1, self.D), dtype=np.float32)
+            n_hist = np.full(self.Hkv, max(L - T, 0), np.int32)
+            kh = rng.standard_normal((self.Hkv, max(L - T, 0), self.D), dtype=np.float32)
+            vh = rng.standard_normal((self.Hkv, max(L - T, 0), self.D), dtype=np.float32)
+            kn = rng.standard_normal((self.Hkv, T, self.D), dtype=np.float32)
+            vn = rng.standard_normal((self.Hkv, T, self.D), dtype=np.float32)
         else:
-            n_hist = np.maximum(self.lens[b].astype(np.int32) - 1, 0)
+            n_hist = np.maximum(self.lens[b].astype(np.int32) - T, 0)
             nmax = int(n_hist.max()) if n_hist.size else 0
             kh = np.zeros((self.Hkv, nmax, self.D), np.float32)
             vh = np.zeros_like(kh)
-            kn = np.zeros((self.Hkv, 1, self.D), np.float32)
+            kn = np.zeros((self.Hkv, T, self.D), np.float32)
             vn = np.zeros_like(kn)
             for h in range(self.Hkv):
                 n = int(n_hist[h])
                 kh[h, :n] = rng.standard_normal((n, self.D), dtype=np.float32)
                 vh[h, :n] = rng.standard_normal((n, self.D), dtype=np.float32)
-                kn[h] = rng.standard_normal((1, self.D), dtype=np.float32)
-                vn[h] = rng.standard_normal((1, self.D), dtype=np.float32)
+                kn[h] = rng.standard_normal((T, self.D), dtype=np.float32)
+                vn[h] = rng.standard_normal((T, self.D), dtype=np.float32)
         return (to_bf16_bits(kh), to_bf16_bits(vh), to_bf16_bits(kn), to_bf16_bits(vn), n_hist)
 
 
@@ -112,13 +119,16 @@ CONFIG_NAMES = {1: "tiny", 2: "llama8b-bf16", 3: "llama8b-fp8-tags", 4: "headwis
 
 
 def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
-                  spare_pages=64, table_width=None):
+                  spare_pages=64, table_width=None, q_len=1):
     """Draw workload `cfg_id` (1..5).
 
     batch / lens / table_width override the workload's own sizes for reduced
     parity cases; stale_frac overrides the fraction of stale expected tags
-    (workload 3 defaults to 0.01, the others to 0).
+    (workload 3 defaults to 0.01, the others to 0); q_len > 1 makes the step
+    a multi-query (speculative verification) step of q_len draft tokens.
     """
+    if not 1 <= int(q_len) <= 8:
+        raise ValueError("q_len must be in 1..8")
     seed = cfg_id if seed is None else seed
     rng = np.random.default_rng(seed)
     spec = {
@@ -150,6 +160,8 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     if spec["layout"] == "head" and L.ndim == 1:
         L = np.repeat(L[:, None], Hkv, axis=1)
     B = L.shape[0]
+    if q_len > 1 and np.any(L < q_len):
+        raise ValueError("every unit of a multi-query step holds its q_len draft tokens")
 
     # 2. pages
     n_rows = L.reshape(-1)
@@ -170,7 +182,8 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     page_tags = rng.integers(0, 2 ** 32, size=P, dtype=np.uint64).astype(np.uint32)
 
     # 4. queries
-    q = to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    qshape = (B, Hq, D) if q_len == 1 else (B, int(q_len), Hq, D)
+    q = to_bf16_bits(rng.standard_normal(qshape, dtype=np.float32))
 
     # 5. expected tags, some stale
     frac = (0.01 if cfg_id == 3 else 0.0) if stale_frac is None else stale_frac
@@ -195,4 +208,4 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
         sigma=np.float32(1.0 / np.sqrt(D)),
         lens=L, block_table=block_table, page_tags=page_tags,
         expected_tags=exp_rows.reshape(block_table.shape),
-        stale=stale_rows.reshape(block_table.shape), q=q, seed=seed)
+        stale=stale_rows.reshape(block_table.shape), q=q, seed=seed, q_len=int(q_len))

@@ -36,6 +36,7 @@ from .paged import (  # noqa: F401
     lse_partial,
     oracle_append,
     oracle_decode,
+    oracle_decode_multi,
     oracle_decode_row,
     oracle_validate,
     units,

@@ -43,6 +43,15 @@ Readings taken where the pages are silent (each is also in the design notes):
   R7 Decode: query head hq uses KV head hq // (Hq / Hkv); scores are
      sigma * q . k over all L tokens; softmax with the max subtracted; a
      flagged sequence, or a unit with L = 0, yields exact zeros.
+  R8 Multi-query decode (speculative verification: the target model checks
+     all draft tokens of a sequence in one forward pass -- "Making Workers AI
+     faster and more efficient", section "Speculative decoding: predicting
+     more than one token"; the extra-large-models write-up, part 4 on
+     speculative decoding).  The T drafts are the last T tokens of each unit,
+     appended before the call; draft t (0-based) sits at position L - T + t
+     and attends tokens 0 .. L - T + t: the whole earlier cache, itself, and
+     the drafts before it.  A draft with no such token (L - T + t < 0) yields
+     zeros, as a flagged sequence does.
 """
 import numpy as np
 
@@ -240,6 +249,28 @@ def oracle_decode(cache, q, block_table, lens, sigma, flags=None):
         for g in range(G):
             hq = h * G + g
             out[b, hq], _ = attention_f64(bf16_to_f64(q[b, hq]), K, V, sigma)
+    return out
+
+
+def oracle_decode_multi(cache, q, block_table, lens, sigma, flags=None):
+    """R8: out[b][t][hq][:] in fp64 for q bf16 bits [B][T][Hq][D]."""
+    B, T, Hq, D = q.shape
+    G = Hq // cache.Hkv
+    out = np.zeros((B, T, Hq, D))
+    for (b, h, row, ph) in units(cache.layout, B, cache.Hkv):
+        if flags is not None and flags[b] != 0:
+            continue
+        L = int(lens[row])
+        if L <= 0:
+            continue
+        K, V = gather_unit(cache, block_table[row], ph, L)
+        for t in range(T):
+            n = L - T + t + 1            # tokens visible to draft t
+            if n <= 0:
+                continue
+            for g in range(G):
+                hq = h * G + g
+                out[b, t, hq], _ = attention_f64(bf16_to_f64(q[b, t, hq]), K[:n], V[:n], sigma)
     return out
 
 

@@ -1,8 +1,9 @@
 """Test helper: build the oracle's cache for a workload by replaying its appends.
 
 A workload's cache is produced the way a decode loop would produce it: one bulk
-append of the first L-1 tokens of each sequence into empty pages, then one
-append of the step's new token.  Only oracle code and the shared input
+append of the first L-T tokens of each sequence into empty pages, then one
+append of the step's T new tokens (T = 1, or the draft tokens of a multi-query
+step).  Only oracle code and the shared input
 generator are used here.
 """
 import numpy as np
@@ -34,11 +35,11 @@ def oracle_fill(w, seqs=None, cache=None):
         if w.layout == "seq":
             zero = np.zeros(1, np.int32)
             n1 = np.array([n_hist[0]], np.int32)
-            one = np.ones(1, np.int32)
+            one = np.full(1, w.q_len, np.int32)
         else:
             zero = np.zeros((1, w.Hkv), np.int32)
             n1 = n_hist[None, :].astype(np.int32)
-            one = np.ones((1, w.Hkv), np.int32)
+            one = np.full((1, w.Hkv), w.q_len, np.int32)
         f1 = oracle_append(cache, bt, zero, n1, k_hist[None], v_hist[None], w.W)
         f2 = oracle_append(cache, bt, n1, one, k_new[None], v_new[None], w.W)
         assert f1[0] == 0 and f2[0] == 0
@@ -60,9 +61,10 @@ def oracle_sequence(w, b):
     The sequence's pages are renumbered 0..n-1 (the result does not depend on
     physical page ids: page-permutation invariance is pinned separately).
     Returns dict(pages=global page ids [n], k, v = local logical pools [n][H][S][D],
-    k_scale, v_scale = [n][H] or None, out = fp64 [Hq][D] (unflagged result)).
+    k_scale, v_scale = [n][H] or None, out = fp64 [Hq][D], or [T][Hq][D] for a
+    multi-query workload (unflagged result)).
     """
-    from oracle import oracle_decode
+    from oracle import oracle_decode, oracle_decode_multi
 
     rows = w.block_table[b:b + 1]
     lens = w.lens[b:b + 1]
@@ -80,7 +82,10 @@ def oracle_sequence(w, b):
     n_pages = max(len(pages), 1)
     sub = _SubWorkload(w, b, local, n_pages)
     cache, _ = oracle_fill(sub, seqs=[0])
-    out = oracle_decode(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
+    if w.q_len == 1:
+        out = oracle_decode(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
+    else:
+        out = oracle_decode_multi(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
     return dict(pages=pages, k=cache.k[:len(pages)], v=cache.v[:len(pages)],
                 k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
                 v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)], out=out)
@@ -95,6 +100,7 @@ class _SubWorkload:
         self.Hkv, self.D, self.P, self.B = w.Hkv, w.D, n_pages, 1
         self.block_table = local_table
         self.lens = w.lens[b:b + 1]
+        self.q_len = w.q_len
 
     def seq_kv(self, _):
         return self._w.seq_kv(self._b)
