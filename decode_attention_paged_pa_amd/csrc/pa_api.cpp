@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: multi-query decode
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -43,9 +43,12 @@ int check_seq(const pa_seq_desc* s) {
   return PA_OK;
 }
 
-int check_heads(const pa_cache_desc* c, int32_t num_q_heads) {
+int check_heads(const pa_cache_desc* c, int32_t num_q_heads, int32_t q_len = 1) {
   if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (num_q_heads / c->num_kv_heads > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (q_len < 1) return PA_ERR_INVALID_ARG;
+  const int group = num_q_heads / c->num_kv_heads;
+  if (group > pa::kMaxGroup || q_len > pa::kMaxQLen) return PA_ERR_UNSUPPORTED;
+  if (q_len > 1 && group * q_len > pa::kMaxCols) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -85,20 +88,21 @@ void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int parts) {
+size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len,
+                     int parts) {
   if (parts <= 1) return 0;
-  const size_t rows = (size_t)s->batch * hq * parts;
+  const size_t rows = (size_t)s->batch * q_len * hq * parts;
   return align256(rows * c->head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
 int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
-                const uint16_t* q, uint16_t* out, float softmax_scale, int32_t num_partitions,
-                uint32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                pa_event_t const* events) {
+                int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
+                int32_t num_partitions, uint32_t* flags, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, pa_event_t const* events) {
   int rc;
   if ((rc = check_cache(cache)) != PA_OK) return rc;
   if ((rc = check_seq(seq)) != PA_OK) return rc;
-  if ((rc = check_heads(cache, num_q_heads)) != PA_OK) return rc;
+  if ((rc = check_heads(cache, num_q_heads, q_len)) != PA_OK) return rc;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return PA_ERR_INVALID_ARG;
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
@@ -106,7 +110,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
   int chunk_pages, parts, ppw;
   choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
-  const size_t need = workspace_for(cache, seq, num_q_heads, parts);
+  const size_t need = workspace_for(cache, seq, num_q_heads, q_len, parts);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
   const bool head = cache->layout == PA_LAYOUT_HEAD;
@@ -144,7 +148,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.q = q;
   a.out = out;
   if (parts > 1) {
-    const size_t rows = (size_t)seq->batch * num_q_heads * parts;
+    const size_t rows = (size_t)seq->batch * q_len * num_q_heads * parts;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align256(rows * cache->head_dim * sizeof(float)));
@@ -153,6 +157,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
+  a.q_len = q_len;
   a.table_width = seq->table_width;
   a.num_pages = cache->num_pages;
   a.chunk_pages = chunk_pages;
@@ -232,7 +237,18 @@ PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, const pa_seq
     return (size_t)-1;
   int cp, parts;
   choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
-  return workspace_for(cache, seq, num_q_heads, parts);
+  return workspace_for(cache, seq, num_q_heads, 1, parts);
+}
+
+PA_API size_t pa_decode_multi_workspace_bytes(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                              int32_t num_q_heads, int32_t q_len,
+                                              int32_t num_partitions) {
+  if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
+      check_heads(cache, num_q_heads, q_len) != PA_OK || num_partitions < 0)
+    return (size_t)-1;
+  int cp, parts;
+  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
+  return workspace_for(cache, seq, num_q_heads, q_len, parts);
 }
 
 PA_API int pa_decode_num_partitions(const pa_cache_desc* cache, const pa_seq_desc* seq,
@@ -251,7 +267,7 @@ PA_API int pa_decode(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t
                      const uint16_t* q, uint16_t* out, float softmax_scale,
                      int32_t num_partitions, uint32_t* flags, void* workspace,
                      size_t workspace_bytes, pa_stream_t stream) {
-  return decode_impl(cache, seq, num_q_heads, q, out, softmax_scale, num_partitions, flags,
+  return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -260,7 +276,24 @@ PA_API int pa_decode_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
                            float softmax_scale, int32_t num_partitions, uint32_t* flags,
                            void* workspace, size_t workspace_bytes, pa_stream_t stream,
                            pa_event_t const events[4]) {
-  return decode_impl(cache, seq, num_q_heads, q, out, softmax_scale, num_partitions, flags,
+  return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events);
+}
+
+PA_API int pa_decode_multi(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                           int32_t num_q_heads, int32_t q_len, const uint16_t* q, uint16_t* out,
+                           float softmax_scale, int32_t num_partitions, uint32_t* flags,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return decode_impl(cache, seq, num_q_heads, q_len, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+PA_API int pa_decode_multi_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                 int32_t num_q_heads, int32_t q_len, const uint16_t* q,
+                                 uint16_t* out, float softmax_scale, int32_t num_partitions,
+                                 uint32_t* flags, void* workspace, size_t workspace_bytes,
+                                 pa_stream_t stream, pa_event_t const events[4]) {
+  return decode_impl(cache, seq, num_q_heads, q_len, q, out, softmax_scale, num_partitions, flags,
                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events);
 }
 
@@ -268,7 +301,9 @@ PA_API const char* pa_strerror(int code) {
   switch (code) {
     case PA_OK: return "success";
     case PA_ERR_INVALID_ARG: return "invalid argument";
-    case PA_ERR_UNSUPPORTED: return "unsupported shape (page_size 16, head_dim 64/128, group <= 16)";
+    case PA_ERR_UNSUPPORTED:
+      return "unsupported shape (page_size 16, head_dim 64/128, group <= 16, q_len <= 8, "
+             "group * q_len <= 64)";
     case PA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown error code";

@@ -41,9 +41,16 @@ constexpr int kPipe = PA_PIPE_DEPTH;
 static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
 
 // BF16 pages hold twice the bytes in the register ring, so that kernel gets
-// one wave per SIMD less than the FP8 one instead of spilling.
+// one wave per SIMD less than the FP8 one instead of spilling; every extra
+// tile of query columns adds its O accumulators and Q operands (D/2 + D/4
+// registers per lane at D = 128... 48 + 16 at D = 64), paid for in waves.
+template <bool FP8, int NQ>
+constexpr int waves_per_eu() {
+  return NQ == 1 ? (FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)
+                 : (NQ == 2 ? (FP8 ? PA_WAVES_PER_EU - 1 : PA_WAVES_PER_EU - 2) : 2);
+}
 #if PA_WAVES_PER_EU > 0
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)))
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(waves_per_eu<FP8, NQ>())))
 #else
 #define PA_OCCUPANCY
 #endif
@@ -111,22 +118,38 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
 // of a workgroup are independent (no LDS, no barrier): each streams its pages
 // through a register ring and writes its own partial (max, sum, O) -- or, with
 // a single partition, the normalised output -- straight from registers.
-template <int D, bool FP8, bool HEAD>
+//
+// Query columns: the G query heads of the unit for each of its T query
+// tokens, column cc = t * G + g, in NQ tiles of 16.  T > 1 is a multi-query
+// step (speculative verification: the drafts are checked in one pass, "Making
+// Workers AI faster and more efficient", speculative decoding section): token
+// t sits at position L - T + t and sees tokens 0 .. L - T + t, so CAUSAL masks
+// the scores of the last page or two per column.  Every K and V fragment is
+// converted once and multiplied into all NQ tiles.
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
 __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
   constexpr int E = FP8 ? 1 : 2;               // bytes per cached element
   constexpr int BLOCK = kPageSize * D * E;     // bytes of one (page, head) block
   constexpr int NSEG = BLOCK / 1024;           // 16-byte loads per lane per block
   constexpr int NT = D / 16;                   // 16-dim output tiles
   constexpr int NSTEP = D / 32;                // QK MFMA steps over d
-  // A wave streams at most two partitions; the state of the first is parked
-  // here (O, max, per-lane sum; one column per lane) until the wave ends.
-  constexpr int kStash = 4 * NT + 2;
+  // A wave streams at most two partitions (single-tile kernels only); the
+  // state of the first is parked here (O, max, per-lane sum; one column per
+  // lane) until the wave ends.
+  constexpr int kStash = NQ == 1 ? 4 * NT + 2 : 1;
   __shared__ float s_stash[kWaves][kStash][64];
+  // With several column tiles the Q operands live in LDS instead of
+  // registers (D/8 registers per tile per lane otherwise): each lane reads
+  // back only what it wrote itself, so no barrier is involved.
+  constexpr bool QLDS = NQ > 1;
+  __shared__ bf16x8 s_q[QLDS ? kWaves : 1][QLDS ? NQ * NSTEP : 1][64];
 
   const int Pn = a.num_parts;
-  const int ppw = a.parts_per_wave;
+  const int ppw = NQ == 1 ? a.parts_per_wave : 1;
   const int groups = (Pn + ppw - 1) / ppw;     // waves per unit
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
+  const int T = CAUSAL ? a.q_len : 1;
+  const int C = G * T;                         // query columns of the unit
   // readfirstlane: the wave index is uniform, and saying so keeps every
   // per-page index, bound and branch in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -170,36 +193,53 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int p0 = part0 * a.chunk_pages;
   const int p1 = min(min(part0 + ppw, Pn) * a.chunk_pages, npages);
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
-  const size_t qrow0 = (size_t)b * Hq + h * G;   // first query row of this unit
+  // query row (in [B][T][Hq]) of column cc of this unit
+  auto col_row = [&](int cc) {
+    const int t = cc / G;
+    return ((size_t)b * T + t) * Hq + h * G + (cc - t * G);
+  };
   if (flagged || p0 >= p1) {
     if (Pn == 1) {  // no reduce follows: this wave owns the output rows
-      for (int i = lane; i < G * D; i += 64) a.out[qrow0 * D + i] = 0;
+      for (int i = lane; i < C * D; i += 64) a.out[col_row(i / D) * D + i % D] = 0;
     }
     return;
   }
   const int n = p1 - p0;
 
-  // Q^T as the B operand of S^T = K Q^T: lane (c, q4) holds query g = c and
-  // the 8 dims that the K A-operand places in this lane for each step.
-  bf16x8 qop[NSTEP];
-  {
-    const uint16_t* qrow = a.q + (qrow0 + (c < G ? c : 0)) * D;
+  // Q^T as the B operand of S^T = K Q^T: lane (c, q4) of tile nq holds column
+  // 16 * nq + c and the 8 dims that the K A-operand places in this lane for
+  // each step.  lim: tokens visible to the lane's column.
+  bf16x8 qop[QLDS ? 1 : NQ][NSTEP];
+  int lim[NQ];
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    const int cc = 16 * nq + c;
+    const bool ok = cc < C;
+    const uint16_t* qrow = a.q + col_row(ok ? cc : 0) * D;
+    lim[nq] = CAUSAL ? L - T + (ok ? cc / G : 0) + 1 : L;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       int d0;
       if (FP8) d0 = 64 * (s >> 1) + 16 * q4 + 8 * (s & 1);
       else d0 = 32 * s + 8 * q4;
       u32x4 v = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if (c >= G) v = u32x4{0u, 0u, 0u, 0u};
-      qop[s] = __builtin_bit_cast(bf16x8, v);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (QLDS) s_q[wave][nq * NSTEP + s][lane] = __builtin_bit_cast(bf16x8, v);
+      else qop[nq][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // first token that some column cannot see: pages at or past it need masks
+  const int vis_min = CAUSAL ? L - T + 1 : L;
 
-  f32x4 o[NT];
+  f32x4 o[NQ][NT];
+  float m_run[NQ], l_acc[NQ];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_acc = 0.f;
+  for (int nq = 0; nq < NQ; ++nq) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) o[nq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[nq] = -INFINITY;
+    l_acc[nq] = 0.f;
+  }
 
   const int32_t* bt = a.block_table + (size_t)row * a.table_width + p0;
   const size_t page_stride = HEAD ? (size_t)BLOCK : (size_t)Hkv * BLOCK;
@@ -265,8 +305,19 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ksc;
-    // ---- scores S^T (token rows x query columns)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Q operand of tile nq, step st; the LDS index carries a per-page zero the
+    // compiler cannot see through, so the reads are not hoisted out of the
+    // page loop (which would put Q back into registers)
+    int qz = 0;
+    if constexpr (QLDS) asm volatile("" : "+v"(qz));
+    auto qv = [&](int nq, int st) -> bf16x8 {
+      if constexpr (QLDS) return s_q[wave][nq * NSTEP + st][lane + qz];
+      else return qop[nq][st];
+    };
+    // ---- scores S^T (token rows x query columns), one accumulator per tile
+    f32x4 acc[NQ];
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) acc[nq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       if (FP8) {
@@ -274,64 +325,80 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         for (int hh = 0; hh < 2; ++hh) {
           u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
           u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
-          u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                        qop[2 * i + hh], acc, 0, 0, 0);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+          for (int nq = 0; nq < NQ; ++nq)
+            acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qv(nq, 2 * i + hh), acc[nq],
+                                                              0, 0, 0);
         }
       } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]), qop[i],
-                                                      acc, 0, 0, 0);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, kr[i]);
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+          acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qv(nq, i), acc[nq], 0, 0, 0);
       }
     }
-    // lane (c, q4) now holds the scores of query c for tokens 4*q4 + r
+    // lane (c, q4) now holds the scores of column c of each tile for tokens 4*q4 + r
     const int tok0 = page * kPageSize + q4 * 4;
-    const bool tail = page * kPageSize + kPageSize > L;
-    float sc[4];
+    const bool tail = page * kPageSize + kPageSize > vis_min;
+    f16x4 pbh[NQ];   // FP8: P^T operands (f16); BF16 uses pbb
+    i16x4 pbb[NQ];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = acc[r] * kfac;
-    if (tail) {
+    for (int nq = 0; nq < NQ; ++nq) {
+      float sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < L) ? sc[r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) sc[r] = acc[nq][r] * kfac;
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim[nq]) ? sc[r] : -INFINITY;
+      }
+      float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mloc = col_max(mloc);
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run[nq] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[nq], mloc);
+        // a column that has seen no token yet keeps -inf on both sides
+        const float alpha = (CAUSAL && m_new == -INFINITY) ? 1.f
+                                                           : __builtin_amdgcn_exp2f(m_run[nq] - m_new);
+        l_acc[nq] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) o[nq][j] *= alpha;
+        m_run[nq] = m_new;
+      }
+      const float mref = (CAUSAL && m_run[nq] == -INFINITY) ? 0.f : m_run[nq];
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - mref);
+      l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
+      if (FP8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pbh[nq][r] = (_Float16)(p[r] * vsc);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pbb[nq][r] = __builtin_bit_cast(short, (__bf16)p[r]);
+      }
     }
-    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mloc = col_max(mloc);
-    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_acc *= alpha;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) o[j] *= alpha;
-      m_run = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
-    l_acc += (p[0] + p[1]) + (p[2] + p[3]);
 
     // ---- O^T += V^T P^T; on the last page zero V of tokens past L (the
     // slots may hold anything, and 0 * NaN would poison the sum)
+    const bool vtail = page * kPageSize + kPageSize > L;
     if (FP8) {
-      f16x4 pb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(p[r] * vsc);
       uint32_t vmask = 0xFFFFFFFFu;
-      if (tail) {
+      if (vtail) {
         const int nv = min(max(L - tok0, 0), 4);
         vmask = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         uint32_t w = vr[j >> 2][j & 3];
-        if (tail) w &= vmask;
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, fp8x4_to_f16x4(w)),
-                                                     pb, o[j], 0, 0, 0);
+        if (vtail) w &= vmask;
+        const f16x4 vf = __builtin_bit_cast(f16x4, fp8x4_to_f16x4(w));
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+          o[nq][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pbh[nq], o[nq][j], 0, 0, 0);
       }
     } else {
-      i16x4 pb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = __builtin_bit_cast(short, (__bf16)p[r]);
       uint64_t vmask = ~0ull;
-      if (tail) {
+      if (vtail) {
         const int nv = min(max(L - tok0, 0), 4);
         vmask = nv >= 4 ? ~0ull : ((1ull << (16 * nv)) - 1ull);
       }
@@ -339,34 +406,43 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       for (int j = 0; j < NT; ++j) {
         const u32x4& seg = vr[j >> 1];
         uint64_t w = ((uint64_t)seg[2 * (j & 1) + 1] << 32) | seg[2 * (j & 1)];
-        if (tail) w &= vmask;
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, w), pb, o[j],
-                                                         0, 0, 0);
+        if (vtail) w &= vmask;
+        const i16x4 vb = __builtin_bit_cast(i16x4, w);
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+          o[nq][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pbb[nq], o[nq][j], 0, 0, 0);
       }
     }
   };
 
   // This wave's result for partition `part`: the normalised output when the
   // unit has a single partition, else the partial (max, sum, unnormalised O).
+  // A column that saw no token (multi-query, L - T + t < 0) has sum 0 and
+  // O = 0, and is written as zeros.
   auto emit = [&](int part) {
-    const float l_tot = col_sum(l_acc);
-    if (c < G) {
-      const size_t qrow = qrow0 + c;
-      if (Pn == 1) {
-        const float inv = 1.f / l_tot;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          uint32_t lo = (uint32_t)bf16_rne(o[j][0] * inv) | ((uint32_t)bf16_rne(o[j][1] * inv) << 16);
-          uint32_t hi = (uint32_t)bf16_rne(o[j][2] * inv) | ((uint32_t)bf16_rne(o[j][3] * inv) << 16);
-          *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
-        }
-      } else {
-        float* po = a.part_o + (qrow * Pn + part) * D;
+    for (int nq = 0; nq < NQ; ++nq) {
+      const float l_tot = col_sum(l_acc[nq]);
+      const int cc = 16 * nq + c;
+      if (cc < C) {
+        const size_t qrow = col_row(cc);
+        if (Pn == 1) {
+          const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = o[j];
-        if (q4 == 0) {
-          a.part_ml[(qrow * Pn + part) * 2 + 0] = m_run;
-          a.part_ml[(qrow * Pn + part) * 2 + 1] = l_tot;
+          for (int j = 0; j < NT; ++j) {
+            const f32x4 v = o[nq][j];
+            uint32_t lo = (uint32_t)bf16_rne(v[0] * inv) | ((uint32_t)bf16_rne(v[1] * inv) << 16);
+            uint32_t hi = (uint32_t)bf16_rne(v[2] * inv) | ((uint32_t)bf16_rne(v[3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
+          }
+        } else {
+          float* po = a.part_o + (qrow * Pn + part) * D;
+#pragma unroll
+          for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = o[nq][j];
+          if (q4 == 0) {
+            a.part_ml[(qrow * Pn + part) * 2 + 0] = m_run[nq];
+            a.part_ml[(qrow * Pn + part) * 2 + 1] = l_tot;
+          }
         }
       }
     }
@@ -409,23 +485,25 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         load(kr[slot], vr[slot], ks[slot], vs[slot], min(r + kPipe - 1, m - 1));
         if (r < m) {
           const int k = seg + r;                   // page within this wave's run
-          if (k == next_boundary) {
-            // Park the finished partition in LDS: a global store now would
-            // be waited for by the next page's throttle, and under the full
-            // read stream stores take long to complete (measured: 6% of the
-            // kernel time on the 32K-token FP8 workload).
+          if constexpr (NQ == 1) {
+            if (k == next_boundary) {
+              // Park the finished partition in LDS: a global store now would
+              // be waited for by the next page's throttle, and under the full
+              // read stream stores take long to complete (measured: 6% of the
+              // kernel time on the 32K-token FP8 workload).
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
+              for (int j = 0; j < NT; ++j)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[j][r];
-            stash[4 * NT][lane] = m_run;
-            stash[4 * NT + 1][lane] = l_acc;
-            ++part;
-            next_boundary += a.chunk_pages;
+                for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[0][j][r];
+              stash[4 * NT][lane] = m_run[0];
+              stash[4 * NT + 1][lane] = l_acc[0];
+              ++part;
+              next_boundary += a.chunk_pages;
 #pragma unroll
-            for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m_run = -INFINITY;
-            l_acc = 0.f;
+              for (int j = 0; j < NT; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+              m_run[0] = -INFINITY;
+              l_acc[0] = 0.f;
+            }
           }
           compute(kr[u], vr[u], ks[u], vs[u], k);
         }
@@ -433,33 +511,40 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   }
   emit(part);
-  if (part > part0) {  // the parked first partition
+  if constexpr (NQ == 1) {
+    if (part > part0) {  // the parked first partition
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[j][r] = stash[4 * j + r][lane];
-    m_run = stash[4 * NT][lane];
-    l_acc = stash[4 * NT + 1][lane];
-    emit(part0);
+        for (int r = 0; r < 4; ++r) o[0][j][r] = stash[4 * j + r][lane];
+      m_run[0] = stash[4 * NT][lane];
+      l_acc[0] = stash[4 * NT + 1][lane];
+      emit(part0);
+    }
   }
 }
 
 // ---------------------------------------------------------------- reduce
-// One workgroup per (sequence, query head); thread d merges dim d over the
-// partitions that hold tokens, in partition order (deterministic).
+// One workgroup per query row (sequence, query token, query head); thread d
+// merges dim d over the partitions that hold tokens visible to the row, in
+// partition order (deterministic).
 template <int D, bool HEAD>
 __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   const int qrow = blockIdx.x;
   const int Hq = a.num_q_heads;
-  const int b = qrow / Hq;
-  const int hq = qrow - b * Hq;
+  const int T = a.q_len;
+  const int b = qrow / (T * Hq);
+  const int rem = qrow - b * T * Hq;
+  const int t = rem / Hq;
+  const int hq = rem - t * Hq;
   const int h = hq / a.group;
   const int row = HEAD ? b * a.num_kv_heads + h : b;
   const int d = threadIdx.x;
   const int cap = a.table_width * kPageSize;
   int L = a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int npages = (L + kPageSize - 1) / kPageSize;
+  const int vis = L - T + t + 1;   // tokens this row sees (T = 1: all L)
+  const int npages = vis > 0 ? (vis + kPageSize - 1) / kPageSize : 0;
   const int nvp = (npages + a.chunk_pages - 1) / a.chunk_pages;
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
   if (flagged || nvp == 0) {
@@ -499,9 +584,10 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   a.out[(size_t)qrow * D + d] = bf16_rne(osum / lsum);
 }
 
-template <int D, bool FP8, bool HEAD>
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  const unsigned groups = (unsigned)(a.num_parts + a.parts_per_wave - 1) / a.parts_per_wave;
+  const int ppw = NQ == 1 ? a.parts_per_wave : 1;
+  const unsigned groups = (unsigned)(a.num_parts + ppw - 1) / ppw;
   unsigned grid;
   if (a.xcd_order) {  // see attention_kernel: (Hkv / 4) workgroups per pair, in blocks of 8 pairs
     const unsigned pairs = (unsigned)a.batch * groups;
@@ -510,8 +596,20 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
     grid = (items + kWaves - 1) / kWaves;
   }
-  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL>), dim3(grid), dim3(64 * kWaves),
+                     0, s, a);
   return hipGetLastError();
+}
+
+// Column tiles: one for plain decode; for T query tokens, ceil(G * T / 16)
+// rounded up to 1, 2 or 4.
+template <int D, bool FP8, bool HEAD>
+hipError_t launch_attention_q(const AttnArgs& a, hipStream_t s) {
+  if (a.q_len == 1) return launch_attention_t<D, FP8, HEAD, 1, false>(a, s);
+  const int cols = a.group * a.q_len;
+  if (cols <= 16) return launch_attention_t<D, FP8, HEAD, 1, true>(a, s);
+  if (cols <= 32) return launch_attention_t<D, FP8, HEAD, 2, true>(a, s);
+  return launch_attention_t<D, FP8, HEAD, 4, true>(a, s);
 }
 
 }  // namespace
@@ -524,19 +622,19 @@ hipError_t launch_validate(const ValidateArgs& a, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,
                             hipStream_t s) {
   if (head_dim == 128) {
-    if (fp8) return head_layout ? launch_attention_t<128, true, true>(a, s)
-                                : launch_attention_t<128, true, false>(a, s);
-    return head_layout ? launch_attention_t<128, false, true>(a, s)
-                       : launch_attention_t<128, false, false>(a, s);
+    if (fp8) return head_layout ? launch_attention_q<128, true, true>(a, s)
+                                : launch_attention_q<128, true, false>(a, s);
+    return head_layout ? launch_attention_q<128, false, true>(a, s)
+                       : launch_attention_q<128, false, false>(a, s);
   }
-  if (fp8) return head_layout ? launch_attention_t<64, true, true>(a, s)
-                              : launch_attention_t<64, true, false>(a, s);
-  return head_layout ? launch_attention_t<64, false, true>(a, s)
-                     : launch_attention_t<64, false, false>(a, s);
+  if (fp8) return head_layout ? launch_attention_q<64, true, true>(a, s)
+                              : launch_attention_q<64, true, false>(a, s);
+  return head_layout ? launch_attention_q<64, false, true>(a, s)
+                     : launch_attention_q<64, false, false>(a, s);
 }
 
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s) {
-  const unsigned grid = (unsigned)a.batch * a.num_q_heads;
+  const unsigned grid = (unsigned)a.batch * a.q_len * a.num_q_heads;
   if (head_dim == 128) {
     if (head_layout) hipLaunchKernelGGL((reduce_kernel<128, true>), dim3(grid), dim3(128), 0, s, a);
     else hipLaunchKernelGGL((reduce_kernel<128, false>), dim3(grid), dim3(128), 0, s, a);

@@ -9,6 +9,8 @@ namespace pa {
 constexpr int kPageSize = 16;      // tokens per page (S)
 constexpr int kWaves = 4;          // waves (independent work items) per attention workgroup
 constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
+constexpr int kMaxQLen = 8;        // query tokens per sequence in one multi-query call
+constexpr int kMaxCols = 64;       // query columns (heads x tokens) per unit: 4 MFMA tiles
 
 // Arguments of the attention (partial) kernel.
 struct AttnArgs {
@@ -19,11 +21,12 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* lens;
   const uint32_t* flags;     // nullptr: nothing flagged
-  const uint16_t* q;
-  uint16_t* out;             // written directly when num_parts == 1
-  float* part_o;             // [B][Hq][Pn][D] unnormalised outputs
-  float* part_ml;            // [B][Hq][Pn][2] running max (log2 domain) and sum
+  const uint16_t* q;         // [B][q_len][Hq][D]
+  uint16_t* out;             // [B][q_len][Hq][D]; written directly when num_parts == 1
+  float* part_o;             // [B][q_len][Hq][Pn][D] unnormalised outputs
+  float* part_ml;            // [B][q_len][Hq][Pn][2] running max (log2 domain) and sum
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
+  int q_len;                 // query tokens per sequence (1: decode; > 1: causal drafts)
   int chunk_pages, num_parts;
   int parts_per_wave;        // consecutive partitions of one unit a wave streams through
   int xcd_order;             // workgroup order that keeps a page's heads on one XCD

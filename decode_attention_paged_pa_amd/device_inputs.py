@@ -35,10 +35,11 @@ class DeviceWorkload:
                   self.v_step, flags=flags)
 
     def decode(self, check=True, num_partitions=0, out=None, workspace=None, events=None):
-        return pa.decode(self.cache, self.q, self.block_table, self.lens, self.w.sigma,
-                         expected_tags=self.expected_tags if check else None,
-                         flags=self.flags if check else None, num_partitions=num_partitions,
-                         out=out, workspace=workspace, events=events)
+        run = pa.decode if self.w.q_len == 1 else pa.decode_multi
+        return run(self.cache, self.q, self.block_table, self.lens, self.w.sigma,
+                   expected_tags=self.expected_tags if check else None,
+                   flags=self.flags if check else None, num_partitions=num_partitions,
+                   out=out, workspace=workspace, events=events)
 
 
 def _dev(x, device, dtype=None):

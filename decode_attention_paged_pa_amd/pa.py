@@ -75,6 +75,14 @@ def lib():
         L.pa_decode_timed.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float, i32,
                                       vp, vp, sz, vp, P(vp)]
         L.pa_decode_timed.restype = ctypes.c_int
+        L.pa_decode_multi.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, vp, vp, ctypes.c_float,
+                                      i32, vp, vp, sz, vp]
+        L.pa_decode_multi.restype = ctypes.c_int
+        L.pa_decode_multi_timed.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, vp, vp,
+                                            ctypes.c_float, i32, vp, vp, sz, vp, P(vp)]
+        L.pa_decode_multi_timed.restype = ctypes.c_int
+        L.pa_decode_multi_workspace_bytes.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, i32]
+        L.pa_decode_multi_workspace_bytes.restype = sz
         L.pa_strerror.argtypes = [ctypes.c_int]
         L.pa_strerror.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
@@ -224,10 +232,38 @@ def num_partitions(cache, block_table, lens, num_q_heads, num_partitions=0):
 def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
            num_partitions=0, out=None, workspace=None, events=None, stream=None):
     """pa_decode: q [B][Hq][D] BF16 -> out [B][Hq][D] BF16 (allocated when None)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][D]")
+    return _decode(cache, q, 1, block_table, lens, softmax_scale, expected_tags, flags,
+                   num_partitions, out, workspace, events, stream)
+
+
+def decode_multi(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
+                 num_partitions=0, out=None, workspace=None, events=None, stream=None):
+    """pa_decode_multi: q [B][T][Hq][D] BF16 (T draft tokens, the last T of each unit,
+    already appended) -> out [B][T][Hq][D] BF16; draft t sees tokens 0 .. L - T + t."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][T][Hq][D]")
+    return _decode(cache, q, q.shape[1], block_table, lens, softmax_scale, expected_tags, flags,
+                   num_partitions, out, workspace, events, stream)
+
+
+def multi_workspace_bytes(cache, block_table, lens, num_q_heads, q_len, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_decode_multi_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                              q_len, num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(-1, "pa_decode_multi_workspace_bytes")
+    return n
+
+
+def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, flags,
+            num_partitions, out, workspace, events, stream):
     sd = _seq(cache, block_table, lens, expected_tags)
     _need(q, "q", BF16)
-    if q.dim() != 3 or q.shape[0] != block_table.shape[0] or q.shape[2] != cache.head_dim:
-        raise ValueError("q must be [B][Hq][D]")
+    if q.shape[0] != block_table.shape[0] or q.shape[-1] != cache.head_dim:
+        raise ValueError("q must be [B](...)[Hq][D] with the table's B and the cache's D")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", BF16)
@@ -238,28 +274,38 @@ def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags
         if flags.numel() != block_table.shape[0]:
             raise ValueError("flags must hold B words")
     cd = cache.desc()
-    Hq = q.shape[1]
-    need = lib().pa_decode_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, num_partitions)
+    Hq = q.shape[-2]
+    L = lib()
+    if q_len == 1:
+        need = L.pa_decode_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, num_partitions)
+    else:
+        need = L.pa_decode_multi_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, q_len,
+                                                 num_partitions)
     if need == ctypes.c_size_t(-1).value:
-        raise PAError(-1, "pa_decode_workspace_bytes")
+        raise PAError(-1, "pa_decode workspace size")
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    args = (ctypes.byref(cd), ctypes.byref(sd), Hq)
+    tail = (_ptr(q), _ptr(out), float(softmax_scale), num_partitions, _ptr(flags), ws_ptr,
+            ws_bytes, _stream(stream))
     if events is None:
-        rc = lib().pa_decode(ctypes.byref(cd), ctypes.byref(sd), Hq, _ptr(q), _ptr(out),
-                             float(softmax_scale), num_partitions, _ptr(flags), ws_ptr, ws_bytes,
-                             _stream(stream))
+        if q_len == 1:
+            rc = L.pa_decode(*args, *tail)
+        else:
+            rc = L.pa_decode_multi(*args, q_len, *tail)
     else:
         for e in events:
             if e is not None and not e.cuda_event:
                 e.record()  # torch creates the underlying hipEvent on first record
         ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
-        rc = lib().pa_decode_timed(ctypes.byref(cd), ctypes.byref(sd), Hq, _ptr(q), _ptr(out),
-                                   float(softmax_scale), num_partitions, _ptr(flags), ws_ptr,
-                                   ws_bytes, _stream(stream), ev)
+        if q_len == 1:
+            rc = L.pa_decode_timed(*args, *tail, ev)
+        else:
+            rc = L.pa_decode_multi_timed(*args, q_len, *tail, ev)
     if rc != 0:
-        raise PAError(rc, "pa_decode")
+        raise PAError(rc, "pa_decode_multi" if q_len > 1 else "pa_decode")
     return out
 
 
@@ -268,7 +314,8 @@ def version():
 
 
 class DecodeStepGraph:
-    """One decode step (append, then decode) captured as a HIP graph and replayed.
+    """One decode step (append, then decode or multi-query decode) captured as a HIP
+    graph and replayed.
 
     The Infire page ("How we built the most efficient inference engine for
     Cloudflare's network", section "Rust-precise CUDA kernels") keeps one graph
@@ -284,7 +331,11 @@ class DecodeStepGraph:
         self.args = (cache, block_table, lens_old, n_new, k_new, v_new, q, lens, softmax_scale,
                      expected_tags, flags, num_partitions)
         self.out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-        need = workspace_bytes(cache, block_table, lens, q.shape[1], num_partitions)
+        if q.dim() == 3:
+            need = workspace_bytes(cache, block_table, lens, q.shape[1], num_partitions)
+        else:
+            need = multi_workspace_bytes(cache, block_table, lens, q.shape[2], q.shape[1],
+                                         num_partitions)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -299,8 +350,9 @@ class DecodeStepGraph:
     def _step(self):
         (cache, bt, lens_old, n_new, k_new, v_new, q, lens, scale, exp, flags, parts) = self.args
         append(cache, bt, lens_old, n_new, k_new, v_new)
-        decode(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
-               out=self.out, workspace=self.workspace)
+        run = decode if q.dim() == 3 else decode_multi
+        run(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
+            out=self.out, workspace=self.workspace)
 
     def replay(self):
         self.graph.replay()

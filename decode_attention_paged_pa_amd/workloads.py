@@ -119,13 +119,14 @@ CONFIG_NAMES = {1: "tiny", 2: "llama8b-bf16", 3: "llama8b-fp8-tags", 4: "headwis
 
 
 def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
-                  spare_pages=64, table_width=None, q_len=1):
+                  spare_pages=64, table_width=None, q_len=1, heads=None):
     """Draw workload `cfg_id` (1..5).
 
     batch / lens / table_width override the workload's own sizes for reduced
     parity cases; stale_frac overrides the fraction of stale expected tags
     (workload 3 defaults to 0.01, the others to 0); q_len > 1 makes the step
-    a multi-query (speculative verification) step of q_len draft tokens.
+    a multi-query (speculative verification) step of q_len draft tokens;
+    heads = (Hq, Hkv) overrides the head counts (edge cases of the grouping).
     """
     if not 1 <= int(q_len) <= 8:
         raise ValueError("q_len must be in 1..8")
@@ -142,6 +143,8 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     B = spec["B"] if batch is None else int(batch)
     W = spec["W"] if table_width is None else int(table_width)
     Hkv, Hq, D = spec["Hkv"], spec["Hq"], spec["D"]
+    if heads is not None:
+        Hq, Hkv = int(heads[0]), int(heads[1])
 
     # 1. lengths
     if lens is not None:

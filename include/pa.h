@@ -203,6 +203,45 @@ int pa_decode_timed(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t 
                     uint32_t *flags, void *workspace, size_t workspace_bytes, pa_stream_t stream,
                     pa_event_t const events[4]);
 
+/*
+ * Multi-query decode: speculative verification of draft tokens.  The target
+ * model checks every candidate token of a sequence in a single forward pass
+ * ("Making Workers AI faster and more efficient", section "Speculative
+ * decoding: predicting more than one token"; the extra-large-models write-up,
+ * part 4, on draft-model speculative decoding).
+ *
+ * q: device BF16 [B][q_len][Hq][D]; out: device BF16 [B][q_len][Hq][D].
+ * The q_len draft tokens are the LAST q_len tokens of every unit: the caller
+ * appends them (pa_cache_append with n_new = q_len) before this call, and
+ * seq->lens counts them.  Query token t (0-based) sits at position
+ * lens[u] - q_len + t and attends tokens 0 .. lens[u] - q_len + t: the
+ * earlier cache, the drafts before it, and itself (causal among the drafts).
+ * A token with nothing to attend (lens[u] - q_len + t < 0) gets +0.0 rows.
+ * Everything else -- scores, softmax, rounding, tag validation, flags,
+ * partitions, workspace alignment -- is as pa_decode; q_len = 1 is pa_decode.
+ *   q_len: 1 .. 8, and (Hq / Hkv) * q_len <= 64 when q_len > 1, else
+ *          PA_ERR_UNSUPPORTED.
+ * Workspace: pa_decode_multi_workspace_bytes(...) bytes (0 with one partition).
+ */
+int pa_decode_multi(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+                    int32_t q_len, const uint16_t *q, uint16_t *out, float softmax_scale,
+                    int32_t num_partitions, uint32_t *flags, void *workspace,
+                    size_t workspace_bytes, pa_stream_t stream);
+
+/* pa_decode_multi with the four timing events of pa_decode_timed. */
+int pa_decode_multi_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                          int32_t num_q_heads, int32_t q_len, const uint16_t *q, uint16_t *out,
+                          float softmax_scale, int32_t num_partitions, uint32_t *flags,
+                          void *workspace, size_t workspace_bytes, pa_stream_t stream,
+                          pa_event_t const events[4]);
+
+/* Workspace bytes of pa_decode_multi; (size_t)-1 for invalid or unsupported
+ * arguments.  The partition count is pa_decode_num_partitions' (q_len does
+ * not change it). */
+size_t pa_decode_multi_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                                       int32_t num_q_heads, int32_t q_len,
+                                       int32_t num_partitions);
+
 /* Static text for a PA_* return code. */
 const char *pa_strerror(int code);
 

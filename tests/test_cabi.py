@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror"):
+    for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror",
+              "pa_decode_multi", "pa_decode_multi_workspace_bytes"):
         assert n in names
 
 
@@ -131,6 +132,36 @@ def test_partition_choice():
     assert n(_seq(batch=4, table_width=32), 0) == 1        # tiny: one partition, no reduce
     assert n(_seq(batch=4, table_width=32), 3) == 3
     assert L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(_seq(table_width=32)), 64, 1) == 0
+
+
+def _decode_multi(cache, seq, hq=32, q_len=4, q=FAKE, out=FAKE, scale=0.088, parts=0, flags=None,
+                  ws=None, ws_bytes=0):
+    L = pa.lib()
+    return L.pa_decode_multi(ctypes.byref(cache), ctypes.byref(seq), hq, q_len, ctypes.c_void_p(q),
+                             ctypes.c_void_p(out), scale, parts,
+                             ctypes.c_void_p(flags) if flags else None,
+                             ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_decode_multi_rejects_bad_arguments():
+    c, s = _cache(), _seq()
+    assert _decode_multi(c, s, q_len=0) == -1
+    assert _decode_multi(c, s, q_len=9) == -2              # more than 8 drafts
+    assert _decode_multi(c, s, hq=8 * 16, q_len=8) == -2   # 16 heads x 8 tokens > 64 columns
+    assert _decode_multi(c, s, hq=8 * 16, q_len=1, parts=4) == -3   # q_len 1: decode's limits
+    assert _decode_multi(c, s, q=FAKE + 8) == -1
+    assert _decode_multi(_cache(head_dim=96), s) == -2
+    assert _decode_multi(c, _seq(expected_tags=FAKE)) == -1
+    L = pa.lib()
+    wsm = lambda hq, t, p: L.pa_decode_multi_workspace_bytes(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(s), hq, t, p)
+    # partials of every (sequence, token, head, partition): D floats + (max, sum)
+    assert wsm(32, 4, 4) == 4 * 4 * 32 * 4 * 128 * 4 + 4 * 4 * 32 * 4 * 2 * 4
+    assert wsm(32, 1, 4) == L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
+    assert wsm(64, 8, 1) == 0
+    assert wsm(8 * 16, 8, 2) == ctypes.c_size_t(-1).value
+    need = wsm(32, 4, 4)
+    assert _decode_multi(c, s, parts=4, ws=FAKE, ws_bytes=need - 1) == -3
 
 
 def test_append_rejects_bad_arguments():
