@@ -16,7 +16,13 @@ are also bracketed by device synchronisation for a wall-clock figure.
 Prints one JSON line.  `value` is the achieved HBM GB/s of the step
 (algorithmic bytes / mean step time); `roofline` is the attention kernel
 against the 8 TB/s HBM peak; `cpu_baseline` is the fp64 oracle's decode on a
-bounded sample of the same workload, on this host's cores.
+bounded sample of the same workload, on this host's cores.  `graph` is the
+same step captured once as a HIP graph and replayed K times (one launch per
+step instead of five).
+
+--q-len T (2..8) turns the step into a multi-query step (speculative
+verification): the append writes T draft tokens per unit and
+pa_decode_multi attends them causally; tokens/s then counts verified tokens.
 """
 import argparse
 import hashlib
@@ -47,17 +53,18 @@ def algorithmic_bytes(w, check=True):
     import numpy as np
 
     e = 1 if w.kv_dtype == "fp8" else 2
+    T = w.q_len
     L = w.lens.astype(np.int64)
     hkv_u = w.Hkv if w.layout == "seq" else 1
     pages = (-(-L // w.S)).sum()
     kv = int(L.sum()) * hkv_u * w.D * 2 * e
-    qo = 2 * w.B * w.Hq * w.D * 2
+    qo = 2 * w.B * T * w.Hq * w.D * 2
     table = 4 * int(pages)
     scales = 8 * int(pages) * hkv_u if e == 1 else 0
     tags = (8 * int(pages) + 4 * w.B) if check else 0
     n_units = w.B * w.Hkv
-    append = n_units * w.D * 2 * (2 + e)
-    attn = kv + w.B * w.Hq * w.D * 2 + table + scales
+    append = n_units * T * w.D * 2 * (2 + e)
+    attn = kv + w.B * T * w.Hq * w.D * 2 + table + scales
     return dict(kv=kv, decode=kv + qo + table + scales + tags, append=append,
                 step=kv + qo + table + scales + tags + append, attention_kernel=attn)
 
@@ -87,14 +94,15 @@ def traffic_from_profile(name, per_launch_units):
 def _oracle_worker(w, seqs, barrier, queue):
     import numpy as np  # noqa: F401
 
-    from oracle import oracle_decode
+    from oracle import oracle_decode, oracle_decode_multi
     from tests.oracle_fill import oracle_fill
 
+    run = oracle_decode if w.q_len == 1 else oracle_decode_multi
     cache, _ = oracle_fill(w, seqs=seqs)           # untimed: building the cache
     barrier.wait()
     t0 = time.perf_counter()
     for b in seqs:
-        oracle_decode(cache, w.q[b:b + 1], w.block_table[b:b + 1], w.lens[b:b + 1], w.sigma)
+        run(cache, w.q[b:b + 1], w.block_table[b:b + 1], w.lens[b:b + 1], w.sigma)
     queue.put(time.perf_counter() - t0)
 
 
@@ -132,11 +140,12 @@ def cpu_baseline(w, n_seqs):
             cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
     except Exception:
         pass
-    return dict(value=len(sample) / wall, unit="tokens/s", cores=cores, kind="oracle",
-                sample="oracle_decode (gather, FP8 dequant, fp64 attention) of %d of the %d "
+    fn = "oracle_decode" if w.q_len == 1 else "oracle_decode_multi (%d drafts)" % w.q_len
+    return dict(value=len(sample) * w.q_len / wall, unit="tokens/s", cores=cores, kind="oracle",
+                sample="%s (gather, FP8 dequant, fp64 attention) of %d of the %d "
                        "sequences (all %d query heads each) of the same workload, one per worker, "
                        "cache build untimed; %.1f s of CPU decode work; %s" % (
-                           len(sample), w.B, w.Hq, sum(times), cpu_model),
+                           fn, len(sample), w.B, w.Hq, sum(times), cpu_model),
                 seconds_wall=wall)
 
 
@@ -147,12 +156,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5, help="workload 2..5")
-    ap.add_argument("--partitions", type=int, default=-1, help="split-K count (-1: 8 for workload 5, else auto)")
+    ap.add_argument("--partitions", type=int, default=-1,
+                    help="split-K count (-1: 8 for workload 5 decode, else the library's choice)")
     ap.add_argument("--no-check", action="store_true", help="no-op tracker: skip the tag check")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="draft tokens per sequence (multi-query step), 1..8")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
     args = ap.parse_args()
@@ -180,20 +193,24 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
         return
-    w = make_workload(args.config, stale_frac=0.0)
-    parts = args.partitions if args.partitions >= 0 else (8 if args.config == 5 else 0)
+    w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len)
+    # split-K 8 is the decode workload's own setting; multi-query steps take the
+    # library's choice (whole grid resident: 4 on the 70B-shaped workload)
+    parts = args.partitions if args.partitions >= 0 else (8 if args.config == 5 and args.q_len == 1
+                                                          else 0)
     check = not args.no_check
-    log("workload %d %s: B=%d Hq=%d Hkv=%d D=%d kv=%s layout=%s tokens=%d" % (
-        w.cfg_id, w.name, w.B, w.Hq, w.Hkv, w.D, w.kv_dtype, w.layout, int(w.lens.sum())))
+    T = w.q_len
+    log("workload %d %s: B=%d Hq=%d Hkv=%d D=%d kv=%s layout=%s tokens=%d q_len=%d" % (
+        w.cfg_id, w.name, w.B, w.Hq, w.Hkv, w.D, w.kv_dtype, w.layout, int(w.lens.sum()), T))
     t0 = time.time()
     dw = build_device_workload(w, device=dev, threads=args.threads, log=log)
     dw.step_append()
     torch.cuda.synchronize()
     log("cache filled in %.1f s" % (time.time() - t0))
     n_parts = pa.num_partitions(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
-    ws_bytes = pa.workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
+    ws_bytes = pa.multi_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(tuple(dw.q.shape), dtype=torch.bfloat16, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -230,14 +247,39 @@ def main():
     by = algorithmic_bytes(w, check)
     gbs = by["step"] / (ms * 1e-3) / 1e9
     attn_gbs = by["attention_kernel"] / (t_attn.mean() * 1e-3) / 1e9
-    tok_s = w.B / (ms * 1e-3)
+    tok_s = w.B * T / (ms * 1e-3)
     log("step %.3f ms (p10 %.3f p90 %.3f); append %.1f us, validate %.1f us, attention %.1f us, "
         "reduce %.1f us; %.0f GB/s step, attention %.0f GB/s (%.1f%% of 8 TB/s)" % (
             ms, np.percentile(t_step, 10), np.percentile(t_step, 90), t_append.mean() * 1e3,
             t_val.mean() * 1e3, t_attn.mean() * 1e3, t_red.mean() * 1e3, gbs, attn_gbs,
             100 * attn_gbs / HBM_PEAK_GBS))
 
-    traffic = traffic_from_profile(w.name, None)
+    graph = None
+    if not args.no_graph:
+        g = pa.DecodeStepGraph(dw.cache, dw.block_table, dw.lens_old, dw.n_step, dw.k_step,
+                               dw.v_step, dw.q, dw.lens, w.sigma,
+                               expected_tags=dw.expected_tags if check else None,
+                               flags=dw.flags if check else None, num_partitions=parts)
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for e in gev:
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        for k in range(K):
+            if not args.no_flush:
+                flush.zero_()
+            gev[k][0].record(stream)
+            g.replay()
+            gev[k][1].record(stream)
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
+        graph = {"ms_per_step": round(g_ms, 4),
+                 "value": round(by["step"] / (g_ms * 1e-3) / 1e9, 1),
+                 "tokens_per_s": round(w.B * T / (g_ms * 1e-3), 1)}
+        log("graph replay: step %.3f ms (%.0f GB/s)" % (g_ms, graph["value"]))
+        del g
+
+    traffic = traffic_from_profile(w.name if T == 1 else "%s-t%d" % (w.name, T), None)
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -253,11 +295,13 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "%s: B=%d, Hq=%d, Hkv=%d, D=%d, page 16, L=%s, %s KV, %s layout, "
-                        "split-K %d, tag check %s" % (
+                        "split-K %d, tag check %s%s" % (
                             w.name, w.B, w.Hq, w.Hkv, w.D,
                             "32768" if args.config == 5 else "drawn",
                             "FP8 e4m3" if w.kv_dtype == "fp8" else "BF16", w.layout.upper(),
-                            n_parts, "on" if check else "off"),
+                            n_parts, "on" if check else "off",
+                            "" if T == 1 else ", %d draft tokens per sequence (causal)" % T),
+            "q_len": T,
             "global_batch": w.B,
             "tokens_attended": int(w.lens.sum()),
             "parallelism": "1 GPU",
@@ -270,6 +314,7 @@ def main():
                        "attention": round(t_attn.mean() * 1e3, 2),
                        "reduce": round(t_red.mean() * 1e3, 2)},
         "algorithmic_bytes": by,
+        "graph": graph,
         "roofline": {
             "bound": "hbm",
             "kernel": "attention_kernel",

@@ -37,8 +37,24 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 4      // occupancy hint for the register allocator (0: none)
 #endif
+// Kernels with several query-column tiles: measured on MI355X, deeper rings
+// and dropping the throttle change nothing there (their time goes to compute
+// and to the lower occupancy), so they keep the same defaults.
+#ifndef PA_MQ_PIPE_DEPTH
+#define PA_MQ_PIPE_DEPTH 2
+#endif
+#ifndef PA_MQ_THROTTLE
+#define PA_MQ_THROTTLE 1
+#endif
+#ifndef PA_MQ_WAVES2
+#define PA_MQ_WAVES2 0         // occupancy hint with 2 column tiles (0: derived below)
+#endif
+#ifndef PA_MQ_WAVES4
+#define PA_MQ_WAVES4 2         // occupancy hint with 4 column tiles
+#endif
 constexpr int kPipe = PA_PIPE_DEPTH;
 static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
+static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
 
 // BF16 pages hold twice the bytes in the register ring, so that kernel gets
 // one wave per SIMD less than the FP8 one instead of spilling; every extra
@@ -47,7 +63,9 @@ static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
 template <bool FP8, int NQ>
 constexpr int waves_per_eu() {
   return NQ == 1 ? (FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)
-                 : (NQ == 2 ? (FP8 ? PA_WAVES_PER_EU - 1 : PA_WAVES_PER_EU - 2) : 2);
+       : NQ == 2 ? (PA_MQ_WAVES2 > 0 ? PA_MQ_WAVES2
+                                     : (FP8 ? PA_WAVES_PER_EU - 1 : PA_WAVES_PER_EU - 2))
+                 : PA_MQ_WAVES4;
 }
 #if PA_WAVES_PER_EU > 0
 #define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(waves_per_eu<FP8, NQ>())))
@@ -133,6 +151,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   constexpr int NSEG = BLOCK / 1024;           // 16-byte loads per lane per block
   constexpr int NT = D / 16;                   // 16-dim output tiles
   constexpr int NSTEP = D / 32;                // QK MFMA steps over d
+  constexpr int PIPE = NQ == 1 ? kPipe : PA_MQ_PIPE_DEPTH;
+  constexpr bool THROTTLE = NQ == 1 ? PA_THROTTLE : PA_MQ_THROTTLE;
   // A wave streams at most two partitions (single-tile kernels only); the
   // state of the first is parked here (O, max, per-lane sum; one column per
   // lane) until the wave ends.
@@ -448,13 +468,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  // Register ring of kPipe pages: page r+kPipe-1 is requested before page r
+  // Register ring of PIPE pages: page r+PIPE-1 is requested before page r
   // is consumed.  Past the end of a segment the last page is requested again
   // (an L2 hit) so that every iteration issues the same loads.  At each
   // partition boundary the finished partition is emitted and the state
   // restarts; the ring keeps streaming across it.
-  u32x4 kr[kPipe][NSEG], vr[kPipe][NSEG];
-  float ks[kPipe], vs[kPipe];
+  u32x4 kr[PIPE][NSEG], vr[PIPE][NSEG];
+  float ks[PIPE], vs[PIPE];
   int part = part0;
   int next_boundary = a.chunk_pages;  // page index (relative to p0) of the next partition
   float (*stash)[64] = s_stash[wave];
@@ -470,19 +490,19 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     asm volatile("" : : "s"(last));
     id_chunk = 0;
 #pragma unroll
-    for (int u = 0; u < kPipe - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1));
-    for (int r0 = 0; r0 < m; r0 += kPipe) {
+    for (int u = 0; u < PIPE - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1));
+    for (int r0 = 0; r0 < m; r0 += PIPE) {
 #pragma unroll
-      for (int u = 0; u < kPipe; ++u) {
+      for (int u = 0; u < PIPE; ++u) {
         const int r = r0 + u;                      // page within the segment
-        const int slot = (u + kPipe - 1) % kPipe;  // a constant once the loop is unrolled
-#if PA_THROTTLE
-        // At most one page in flight per wave besides the one being consumed:
-        // measured on MI355X, 2048 waves each keeping two or more pages of
-        // random 2 KiB blocks outstanding move the cache 2-4% slower.
-        __builtin_amdgcn_s_waitcnt(0x0F70);        // s_waitcnt vmcnt(0)
-#endif
-        load(kr[slot], vr[slot], ks[slot], vs[slot], min(r + kPipe - 1, m - 1));
+        const int slot = (u + PIPE - 1) % PIPE;  // a constant once the loop is unrolled
+        if constexpr (THROTTLE) {
+          // At most one page in flight per wave besides the one being consumed:
+          // measured on MI355X, 2048 waves each keeping two or more pages of
+          // random 2 KiB blocks outstanding move the cache 2-4% slower.
+          __builtin_amdgcn_s_waitcnt(0x0F70);      // s_waitcnt vmcnt(0)
+        }
+        load(kr[slot], vr[slot], ks[slot], vs[slot], min(r + PIPE - 1, m - 1));
         if (r < m) {
           const int k = seg + r;                   // page within this wave's run
           if constexpr (NQ == 1) {
