@@ -35,9 +35,12 @@ from .paged import (  # noqa: F401
     lse_merge,
     lse_partial,
     oracle_append,
+    oracle_attention_mass,
+    oracle_compact,
     oracle_decode,
     oracle_decode_multi,
     oracle_decode_row,
+    oracle_score_update,
     oracle_validate,
     units,
 )

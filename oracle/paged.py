@@ -52,6 +52,21 @@ Readings taken where the pages are silent (each is also in the design notes):
      and attends tokens 0 .. L - T + t: the whole earlier cache, itself, and
      the drafts before it.  A draft with no such token (L - T + t < 0) yields
      zeros, as a flagged sequence does.
+  R9 Eviction score (KV-compression page, section "KV cache compression goes
+     open source": evict the KV entries with the lowest accumulated past
+     attention, like a least-frequently-used policy; the per-head block table
+     lets heads be compressed at different rates).  The score of a cached
+     token of a (sequence, KV head) grows at each decode step by the softmax
+     weight the step puts on it, summed over the G query heads of the group.
+     Scores are fp32, one per physical (page, head, slot), so they travel with
+     the page.  Flagged sequences and slots past L are not updated.
+  R10 Compaction after eviction: the tokens a unit keeps (strictly increasing
+     positions) are written, in order, from position 0 into the pages of a new
+     table.  BF16 values are copied.  FP8 values are first decoded under their
+     old page scale, x = fl32(dec(c) * s_old), then quantised into the new
+     page as an append of fresh pages does (R2, R3): s = fl32(amax / 448) over
+     the page's x, codes RNE(sat(fl32(x / s))).  Scores are copied with their
+     tokens.
 """
 import numpy as np
 
@@ -272,6 +287,86 @@ def oracle_decode_multi(cache, q, block_table, lens, sigma, flags=None):
                 hq = h * G + g
                 out[b, t, hq], _ = attention_f64(bf16_to_f64(q[b, t, hq]), K[:n], V[:n], sigma)
     return out
+
+
+# ------------------------------------------------------ eviction scores
+def oracle_attention_mass(cache, q, block_table, lens, sigma, flags=None):
+    """R9: per unit, the step's attention mass on each of its L tokens.
+
+    Returns {(b, h): fp64 [L]} = sum over the G query heads of the unit of the
+    softmax weights (each head's weights sum to 1, so the masses sum to G).
+    Flagged sequences and empty units are absent.
+    """
+    B, Hq, D = q.shape
+    G = Hq // cache.Hkv
+    mass = {}
+    for (b, h, row, ph) in units(cache.layout, B, cache.Hkv):
+        if flags is not None and flags[b] != 0:
+            continue
+        L = int(lens[row])
+        if L <= 0:
+            continue
+        K, V = gather_unit(cache, block_table[row], ph, L)
+        m = np.zeros(L)
+        for g in range(G):
+            _, wts = attention_f64(bf16_to_f64(q[b, h * G + g]), K, V, sigma)
+            m += wts
+        mass[(b, h)] = m
+    return mass
+
+
+def oracle_score_update(layout, scores, block_table, lens, mass, page_size):
+    """Add the masses to the paged score array (fp32 [P][heads][S]) in place.
+
+    The sum is taken in fp64 and rounded once to fp32 per slot.
+    """
+    for (b, h), m in mass.items():
+        row = (b,) if layout == "seq" else (b, h)
+        ph = h if layout == "seq" else 0
+        for t in range(len(m)):
+            pid = int(block_table[row][t // page_size])
+            slot = t % page_size
+            scores[pid, ph, slot] = np.float32(np.float64(scores[pid, ph, slot]) + m[t])
+    return scores
+
+
+# ------------------------------------------------------------ compaction
+def oracle_compact(cache, block_table, lens, keep, n_keep, new_table, scores=None):
+    """R10: rewrite each unit's kept tokens into the pages of new_table.
+
+    keep: int32 [units][max_keep] strictly increasing positions (< L) of the
+    tokens a unit keeps, n_keep [units] how many; units are in unit order
+    (SEQ: (b, h) with b outer; HEAD: the same).  new_table has the old table's
+    layout and never names a page the old table reads.  Returns the new
+    cache (a copy) and the new scores (a copy) or None.
+    """
+    c = cache.copy()
+    new_scores = None if scores is None else scores.copy()
+    S, D = cache.S, cache.D
+    B = block_table.shape[0]
+    for i, (b, h, row, ph) in enumerate(units(cache.layout, B, cache.Hkv)):
+        n = int(n_keep[i])
+        pos = [int(x) for x in keep[i][:n]]
+        for p0 in range(0, n, S):
+            chunk = pos[p0:p0 + S]
+            pid_new = int(new_table[row][p0 // S])
+            src = [(int(block_table[row][t // S]), t % S) for t in chunk]
+            slots = np.arange(len(chunk))
+            for pool_old, pool_new, sc_old, sc_new in ((cache.k, c.k, cache.k_scale, c.k_scale),
+                                                       (cache.v, c.v, cache.v_scale, c.v_scale)):
+                if cache.kv_dtype == "bf16":
+                    pool_new[pid_new, ph, slots] = [pool_old[p, ph, sl] for p, sl in src]
+                    continue
+                x = np.stack([(e4m3_to_f64(pool_old[p, ph, sl]).astype(np.float32)
+                               * sc_old[p, ph]).astype(np.float32) for p, sl in src])
+                amax = np.float32(np.max(np.abs(x)))
+                s_new = np.float32(amax / E4M3_MAX_F32)
+                pool_new[pid_new, ph, slots] = _quantise(x, s_new)
+                sc_new[pid_new, ph] = s_new
+            if scores is not None:
+                for j, (p, sl) in enumerate(src):
+                    new_scores[pid_new, ph, j] = scores[p, ph, sl]
+    return c, new_scores
 
 
 def lse_partial(q, K, V, sigma):
