@@ -23,6 +23,9 @@ step instead of five).
 --q-len T (2..8) turns the step into a multi-query step (speculative
 verification): the append writes T draft tokens per unit and
 pa_decode_multi attends them causally; tokens/s then counts verified tokens.
+--scored makes the decode a scored decode (eviction scores updated in place).
+--compact F times pa_cache_compact keeping a fraction F of every unit's
+tokens (random positions) into spare pages, and reports its GB/s instead.
 """
 import argparse
 import hashlib
@@ -42,7 +45,7 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, check=True):
+def algorithmic_bytes(w, check=True, scored=False):
     """Bytes the method must move for one decode step (append + decode).
 
     Decode: every attended token's K and V once (L x Hkv_u x D x 2 x e), Q in and
@@ -65,8 +68,21 @@ def algorithmic_bytes(w, check=True):
     n_units = w.B * w.Hkv
     append = n_units * T * w.D * 2 * (2 + e)
     attn = kv + w.B * T * w.Hq * w.D * 2 + table + scales
-    return dict(kv=kv, decode=kv + qo + table + scales + tags, append=append,
-                step=kv + qo + table + scales + tags + append, attention_kernel=attn)
+    score = 8 * int(L.sum()) * hkv_u if scored else 0     # read-modify-write of one fp32 per token
+    return dict(kv=kv, decode=kv + qo + table + scales + tags + score, append=append,
+                step=kv + qo + table + scales + tags + append + score, attention_kernel=attn,
+                scores=score)
+
+
+def compaction_bytes(w, n_keep_units):
+    """Bytes pa_cache_compact must move: every kept token's K and V read and
+    written once (plus, for FP8, the source scales read and the new ones written)."""
+    e = 1 if w.kv_dtype == "fp8" else 2
+    kept = int(n_keep_units.sum())
+    b = 2 * kept * w.D * 2 * e
+    if e == 1:
+        b += 2 * 4 * kept + 2 * 4 * -(-kept // w.S)
+    return b
 
 
 def kernel_source_sha():
@@ -149,6 +165,85 @@ def cpu_baseline(w, n_seqs):
                 seconds_wall=wall)
 
 
+# ---------------------------------------------------------------- compaction
+def bench_compaction(args):
+    """pa_cache_compact on a workload with enough spare pages: every unit keeps a
+    random fraction of its tokens (increasing positions), written to fresh pages."""
+    import numpy as np
+    import torch
+
+    from decode_attention_paged_pa_amd import pa
+    from decode_attention_paged_pa_amd.device_inputs import build_device_workload
+    from decode_attention_paged_pa_amd.workloads import make_workload
+
+    frac = args.compact
+    probe = make_workload(args.config, stale_frac=0.0)
+    used = probe.n_pages_used()
+    w = make_workload(args.config, stale_frac=0.0,
+                      spare_pages=int(used * frac) + probe.B * probe.Hkv + 64)
+    log("compaction to %.4f of the tokens: workload %d %s, P=%d" % (frac, w.cfg_id, w.name, w.P))
+    dw = build_device_workload(w, threads=args.threads, log=log)
+    dw.step_append()
+    rng = np.random.default_rng(7)
+    lens_u = w.lens.reshape(-1) if w.layout == "head" else np.repeat(w.lens, w.Hkv)
+    if w.layout == "seq":
+        n_keep = np.maximum(1, (w.lens * frac).astype(np.int32))
+        n_units = np.repeat(n_keep, w.Hkv)
+    else:
+        n_keep = np.maximum(1, (w.lens * frac).astype(np.int32))
+        n_units = n_keep.reshape(-1)
+    K = int(n_units.max())
+    keep = np.zeros((w.B * w.Hkv, K), np.int32)
+    for u in range(w.B * w.Hkv):
+        n = int(n_units[u])
+        keep[u, :n] = np.sort(rng.choice(int(lens_u[u]), n, replace=False))
+    keep = keep.reshape(w.B, w.Hkv, K)
+    used_pages = set(w.block_table[w.block_table != 0x7FFFFFFF].tolist())
+    free = np.array([p for p in range(w.P) if p not in used_pages], np.int32)
+    nt = np.full(w.block_table.shape, 0x7FFFFFFF, np.int32)
+    k = 0
+    rows = [(b,) for b in range(w.B)] if w.layout == "seq" else [
+        (b, h) for b in range(w.B) for h in range(w.Hkv)]
+    for row in rows:
+        need = -(-int(n_keep[row]) // w.S)
+        nt[row][:need] = free[k:k + need]
+        k += need
+    keep_d = torch.from_numpy(keep).cuda()
+    n_keep_d = torch.from_numpy(n_keep.astype(np.int32)).cuda()
+    nt_d = torch.from_numpy(nt).cuda()
+    scores = dw.cache.new_scores()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        pa.compact(dw.cache, dw.block_table, dw.lens, keep_d, n_keep_d, nt_d, scores=scores)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(args.steps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pa.compact(dw.cache, dw.block_table, dw.lens, keep_d, n_keep_d, nt_d, scores=scores)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.mean(ts))
+    by = compaction_bytes(w, n_units) + 8 * int(n_units.sum())   # + the scores moved
+    gbs = by / (ms * 1e-3) / 1e9
+    log("compaction: %.3f ms, %d tokens kept of %d, %.0f GB/s (%.1f%% of 8 TB/s)" % (
+        ms, int(n_units.sum()), int(lens_u.sum()), gbs, gbs / 80))
+    print(json.dumps({
+        "metric": "KV compaction after eviction: achieved HBM GB/s", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": "%s, keep %.4f of every unit's tokens (random positions), "
+                               "scores moved" % (w.name, frac), "global_batch": w.B},
+        "algorithmic_bytes": by,
+        "roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -166,6 +261,9 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="draft tokens per sequence (multi-query step), 1..8")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--scored", action="store_true", help="scored decode (eviction scores)")
+    ap.add_argument("--compact", type=float, default=0.0,
+                    help="time compaction to this fraction of the tokens instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
     args = ap.parse_args()
@@ -193,6 +291,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
         return
+    if args.compact > 0:
+        return bench_compaction(args)
     w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len)
     # split-K 8 is the decode workload's own setting; multi-query steps take the
     # library's choice (whole grid resident: 4 on the 70B-shaped workload)
@@ -208,7 +308,11 @@ def main():
     torch.cuda.synchronize()
     log("cache filled in %.1f s" % (time.time() - t0))
     n_parts = pa.num_partitions(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
-    ws_bytes = pa.multi_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
+    if args.scored:
+        ws_bytes = pa.scored_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
+        scores = dw.cache.new_scores()
+    else:
+        ws_bytes = pa.multi_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty(tuple(dw.q.shape), dtype=torch.bfloat16, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -218,8 +322,14 @@ def main():
         if evs is not None:
             evs[0].record(stream)
         dw.step_append()
-        dw.decode(check=check, num_partitions=parts, out=out, workspace=workspace,
-                  events=None if evs is None else evs[1:])
+        if args.scored:
+            pa.decode_scored(dw.cache, dw.q, dw.block_table, dw.lens, w.sigma, scores,
+                             expected_tags=dw.expected_tags if check else None,
+                             flags=dw.flags if check else None, num_partitions=parts, out=out,
+                             workspace=workspace, events=None if evs is None else evs[1:])
+        else:
+            dw.decode(check=check, num_partitions=parts, out=out, workspace=workspace,
+                      events=None if evs is None else evs[1:])
 
     for _ in range(args.warmup):
         step()
@@ -244,18 +354,19 @@ def main():
     t_attn = np.array([e[2].elapsed_time(e[3]) for e in evs])
     t_red = np.array([e[3].elapsed_time(e[4]) for e in evs])
     ms = float(t_step.mean())
-    by = algorithmic_bytes(w, check)
+    by = algorithmic_bytes(w, check, args.scored)
     gbs = by["step"] / (ms * 1e-3) / 1e9
     attn_gbs = by["attention_kernel"] / (t_attn.mean() * 1e-3) / 1e9
     tok_s = w.B * T / (ms * 1e-3)
     log("step %.3f ms (p10 %.3f p90 %.3f); append %.1f us, validate %.1f us, attention %.1f us, "
-        "reduce %.1f us; %.0f GB/s step, attention %.0f GB/s (%.1f%% of 8 TB/s)" % (
+        "reduce%s %.1f us; %.0f GB/s step, attention %.0f GB/s (%.1f%% of 8 TB/s)" % (
             ms, np.percentile(t_step, 10), np.percentile(t_step, 90), t_append.mean() * 1e3,
-            t_val.mean() * 1e3, t_attn.mean() * 1e3, t_red.mean() * 1e3, gbs, attn_gbs,
+            t_val.mean() * 1e3, t_attn.mean() * 1e3, " + score" if args.scored else "",
+            t_red.mean() * 1e3, gbs, attn_gbs,
             100 * attn_gbs / HBM_PEAK_GBS))
 
     graph = None
-    if not args.no_graph:
+    if not args.no_graph and not args.scored:
         g = pa.DecodeStepGraph(dw.cache, dw.block_table, dw.lens_old, dw.n_step, dw.k_step,
                                dw.v_step, dw.q, dw.lens, w.sigma,
                                expected_tags=dw.expected_tags if check else None,
@@ -300,7 +411,8 @@ def main():
                             "32768" if args.config == 5 else "drawn",
                             "FP8 e4m3" if w.kv_dtype == "fp8" else "BF16", w.layout.upper(),
                             n_parts, "on" if check else "off",
-                            "" if T == 1 else ", %d draft tokens per sequence (causal)" % T),
+                            ("" if T == 1 else ", %d draft tokens per sequence (causal)" % T)
+                            + (", eviction scores updated" if args.scored else "")),
             "q_len": T,
             "global_batch": w.B,
             "tokens_attended": int(w.lens.sum()),
@@ -312,7 +424,7 @@ def main():
         "kernels_us": {"append": round(t_append.mean() * 1e3, 2),
                        "validate": round(t_val.mean() * 1e3, 2),
                        "attention": round(t_attn.mean() * 1e3, 2),
-                       "reduce": round(t_red.mean() * 1e3, 2)},
+                       ("reduce+score" if args.scored else "reduce"): round(t_red.mean() * 1e3, 2)},
         "algorithmic_bytes": by,
         "graph": graph,
         "roofline": {

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: multi-query decode
+constexpr int kVersion = 300;  // 0.3.0: eviction scores and compaction
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -88,17 +88,45 @@ void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Partials [B][T][Hq][Pn] (D floats, then (max, sum)) when Pn > 1; for a
+// scored decode also the page scores [units][W][G][16] and the rows' final
+// (max, sum) [B][Hq][2].
+struct WorkspaceLayout {
+  size_t part_o = 0, part_ml = 0, logits = 0, row_ml = 0, total = 0;
+};
+
+WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
+                                 int32_t q_len, int parts, bool scored) {
+  WorkspaceLayout w;
+  size_t off = 0;
+  if (parts > 1) {
+    const size_t rows = (size_t)s->batch * q_len * hq * parts;
+    w.part_o = off;
+    off += align256(rows * c->head_dim * sizeof(float));
+    w.part_ml = off;
+    off += align256(rows * 2 * sizeof(float));
+  }
+  if (scored) {
+    const size_t units = (size_t)s->batch * c->num_kv_heads;
+    const size_t group = (size_t)hq / c->num_kv_heads;
+    w.logits = off;
+    off += align256(units * s->table_width * group * pa::kPageSize * sizeof(float));
+    w.row_ml = off;
+    off += align256((size_t)s->batch * hq * 2 * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
 size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len,
-                     int parts) {
-  if (parts <= 1) return 0;
-  const size_t rows = (size_t)s->batch * q_len * hq * parts;
-  return align256(rows * c->head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+                     int parts, bool scored = false) {
+  return workspace_layout(c, s, hq, q_len, parts, scored).total;
 }
 
 int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
                 int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
                 int32_t num_partitions, uint32_t* flags, void* workspace, size_t workspace_bytes,
-                hipStream_t stream, pa_event_t const* events) {
+                hipStream_t stream, pa_event_t const* events, float* scores = nullptr) {
   int rc;
   if ((rc = check_cache(cache)) != PA_OK) return rc;
   if ((rc = check_seq(seq)) != PA_OK) return rc;
@@ -108,9 +136,12 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
   if (seq->expected_tags && (!flags || !cache->page_tags)) return PA_ERR_INVALID_ARG;
   if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
+  if (scores && (q_len != 1 || !aligned(scores, 4))) return PA_ERR_INVALID_ARG;
   int chunk_pages, parts, ppw;
   choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
-  const size_t need = workspace_for(cache, seq, num_q_heads, q_len, parts);
+  const WorkspaceLayout wl =
+      workspace_layout(cache, seq, num_q_heads, q_len, parts, scores != nullptr);
+  const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
   const bool head = cache->layout == PA_LAYOUT_HEAD;
@@ -147,11 +178,14 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.flags = flags;
   a.q = q;
   a.out = out;
+  char* ws = static_cast<char*>(workspace);
   if (parts > 1) {
-    const size_t rows = (size_t)seq->batch * q_len * num_q_heads * parts;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         align256(rows * cache->head_dim * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(ws + wl.part_o);
+    a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
+  }
+  if (scores) {
+    a.logits = reinterpret_cast<float*>(ws + wl.logits);
+    a.row_ml = reinterpret_cast<float*>(ws + wl.row_ml);
   }
   a.batch = seq->batch;
   a.num_q_heads = num_q_heads;
@@ -175,6 +209,23 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   rec(2);
   if (parts > 1) {
     if (pa::launch_reduce(a, cache->head_dim, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (scores) {
+    pa::ScoreArgs sa{};
+    sa.logits = a.logits;
+    sa.row_ml = a.row_ml;
+    sa.block_table = seq->block_table;
+    sa.lens = seq->lens;
+    sa.flags = flags;
+    sa.scores = scores;
+    sa.batch = seq->batch;
+    sa.num_kv_heads = cache->num_kv_heads;
+    sa.group = a.group;
+    sa.num_q_heads = num_q_heads;
+    sa.table_width = seq->table_width;
+    sa.num_pages = cache->num_pages;
+    sa.head_layout = head;
+    if (pa::launch_score(sa, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   rec(3);
   return PA_OK;
@@ -278,6 +329,78 @@ PA_API int pa_decode_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
                            pa_event_t const events[4]) {
   return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events);
+}
+
+PA_API size_t pa_decode_scored_workspace_bytes(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                               int32_t num_q_heads, int32_t num_partitions) {
+  if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
+      check_heads(cache, num_q_heads) != PA_OK || num_partitions < 0)
+    return (size_t)-1;
+  int cp, parts;
+  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
+  return workspace_for(cache, seq, num_q_heads, 1, parts, true);
+}
+
+PA_API int pa_decode_scored(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                            int32_t num_q_heads, const uint16_t* q, uint16_t* out,
+                            float softmax_scale, int32_t num_partitions, uint32_t* flags,
+                            float* scores, void* workspace, size_t workspace_bytes,
+                            pa_stream_t stream) {
+  if (!scores) return PA_ERR_INVALID_ARG;
+  return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr,
+                     scores);
+}
+
+PA_API int pa_decode_scored_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                  int32_t num_q_heads, const uint16_t* q, uint16_t* out,
+                                  float softmax_scale, int32_t num_partitions, uint32_t* flags,
+                                  float* scores, void* workspace, size_t workspace_bytes,
+                                  pa_stream_t stream, pa_event_t const events[4]) {
+  if (!scores) return PA_ERR_INVALID_ARG;
+  return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events,
+                     scores);
+}
+
+PA_API int pa_cache_compact(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                            const int32_t* keep, int32_t keep_stride, const int32_t* n_keep,
+                            const int32_t* new_table, float* scores, uint32_t* flags,
+                            pa_stream_t stream) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  if (keep_stride <= 0 || !keep || !n_keep || !new_table) return PA_ERR_INVALID_ARG;
+  if (!aligned(keep, 4) || !aligned(n_keep, 4) || !aligned(new_table, 4)) return PA_ERR_INVALID_ARG;
+  if ((scores && !aligned(scores, 4)) || (flags && !aligned(flags, 4))) return PA_ERR_INVALID_ARG;
+  pa::CompactArgs a{};
+  a.k_old = static_cast<const uint8_t*>(cache->k_pages);
+  a.v_old = static_cast<const uint8_t*>(cache->v_pages);
+  a.k_new = static_cast<uint8_t*>(cache->k_pages);
+  a.v_new = static_cast<uint8_t*>(cache->v_pages);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = seq->block_table;
+  a.lens = seq->lens;
+  a.keep = keep;
+  a.n_keep = n_keep;
+  a.new_table = new_table;
+  a.scores = scores;
+  a.flags = flags;
+  a.batch = seq->batch;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.table_width = seq->table_width;
+  a.num_pages = cache->num_pages;
+  a.keep_stride = keep_stride;
+  a.pages_per_unit = (keep_stride + pa::kPageSize - 1) / pa::kPageSize;
+  a.head_layout = cache->layout == PA_LAYOUT_HEAD;
+  a.fp8 = cache->kv_dtype == PA_KV_FP8_E4M3;
+  const int64_t grid = (int64_t)a.batch * a.num_kv_heads * a.pages_per_unit;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (pa::launch_compact(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
 }
 
 PA_API int pa_decode_multi(const pa_cache_desc* cache, const pa_seq_desc* seq,

@@ -144,7 +144,18 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
 // t sits at position L - T + t and sees tokens 0 .. L - T + t, so CAUSAL masks
 // the scores of the last page or two per column.  Every K and V fragment is
 // converted once and multiplied into all NQ tiles.
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
+//
+// SCORE (decode only) also writes every page's log2-domain scores, and the
+// final (max, sum) of single-partition rows, for the eviction score update
+// ("Making Workers AI faster and more efficient", KV cache compression
+// section: evict the entries with the least accumulated attention).  The
+// weights themselves need the final max and sum of the whole row, known only
+// after the reduce, so the scores go out and a later kernel normalises them.
+// Measured on the 32K-token FP8 workload, that write stream (G * 64 bytes per
+// page and head, 537 MB) costs about 45% of the kernel time whatever its
+// shape: per-page stores, 8 KiB bursts gathered in LDS, non-temporal stores
+// and half the bytes all land within 10% of each other.
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SCORE = false>
 __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
   constexpr int E = FP8 ? 1 : 2;               // bytes per cached element
   constexpr int BLOCK = kPageSize * D * E;     // bytes of one (page, head) block
@@ -372,6 +383,12 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim[nq]) ? sc[r] : -INFINITY;
       }
+      if constexpr (SCORE) {
+        // [unit][page][g][16 tokens]: the valid columns' lanes write one 16-byte chunk each
+        if (c < G)
+          *reinterpret_cast<f32x4*>(a.logits + (((size_t)unit * a.table_width + page) * G + c) * 16 +
+                                    4 * q4) = f32x4{sc[0], sc[1], sc[2], sc[3]};
+      }
       float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mloc = col_max(mloc);
       if (__builtin_amdgcn_ballot_w64(mloc > m_run[nq] + kRescaleSlack)) {
@@ -447,6 +464,12 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       if (cc < C) {
         const size_t qrow = col_row(cc);
         if (Pn == 1) {
+          if constexpr (SCORE) {
+            if (q4 == 0) {
+              a.row_ml[qrow * 2 + 0] = m_run[nq];
+              a.row_ml[qrow * 2 + 1] = l_tot;
+            }
+          }
           const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
@@ -602,9 +625,13 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
     M = Mg;
   }
   a.out[(size_t)qrow * D + d] = bf16_rne(osum / lsum);
+  if (a.row_ml != nullptr && d == 0) {   // scored decode: the row's final (max, sum)
+    a.row_ml[(size_t)qrow * 2 + 0] = M;
+    a.row_ml[(size_t)qrow * 2 + 1] = lsum;
+  }
 }
 
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SCORE = false>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   const int ppw = NQ == 1 ? a.parts_per_wave : 1;
   const unsigned groups = (unsigned)(a.num_parts + ppw - 1) / ppw;
@@ -616,8 +643,8 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
     grid = (items + kWaves - 1) / kWaves;
   }
-  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL>), dim3(grid), dim3(64 * kWaves),
-                     0, s, a);
+  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL, SCORE>), dim3(grid),
+                     dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -625,6 +652,7 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
 // rounded up to 1, 2 or 4.
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_attention_q(const AttnArgs& a, hipStream_t s) {
+  if (a.logits) return launch_attention_t<D, FP8, HEAD, 1, false, true>(a, s);  // decode only
   if (a.q_len == 1) return launch_attention_t<D, FP8, HEAD, 1, false>(a, s);
   const int cols = a.group * a.q_len;
   if (cols <= 16) return launch_attention_t<D, FP8, HEAD, 1, true>(a, s);

@@ -27,6 +27,8 @@ struct AttnArgs {
   float* part_ml;            // [B][q_len][Hq][Pn][2] running max (log2 domain) and sum
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int q_len;                 // query tokens per sequence (1: decode; > 1: causal drafts)
+  float* logits;             // scored decode: [units][W][G][16] log2-domain scores, else nullptr
+  float* row_ml;             // scored decode: [B][Hq][2] final max (log2) and sum per row
   int chunk_pages, num_parts;
   int parts_per_wave;        // consecutive partitions of one unit a wave streams through
   int xcd_order;             // workgroup order that keeps a page's heads on one XCD
@@ -59,6 +61,40 @@ struct AppendArgs {
   bool head_layout, fp8;
 };
 
+// Eviction score update: adds each token's attention mass (softmax weights
+// summed over the G query heads of its KV head) to the paged score array.
+struct ScoreArgs {
+  const float* logits;       // as AttnArgs::logits
+  const float* row_ml;       // as AttnArgs::row_ml
+  const int32_t* block_table;
+  const int32_t* lens;
+  const uint32_t* flags;     // nullptr: nothing flagged
+  float* scores;             // [P][Hkv (SEQ) or 1 (HEAD)][S]
+  int batch, num_kv_heads, group, num_q_heads, table_width, num_pages;
+  bool head_layout;
+};
+
+// Compaction after eviction: the kept tokens of each unit, in list order, are
+// rewritten from position 0 into the pages of a new table.
+struct CompactArgs {
+  const uint8_t* k_old;      // pools (the same allocations as k_new / v_new)
+  const uint8_t* v_old;
+  uint8_t* k_new;
+  uint8_t* v_new;
+  float* k_scale;            // FP8 only
+  float* v_scale;
+  const int32_t* block_table;  // old table
+  const int32_t* lens;         // old lengths
+  const int32_t* keep;         // [B][Hkv][keep_stride] positions to keep
+  const int32_t* n_keep;       // lens' shape
+  const int32_t* new_table;    // the old table's shape
+  float* scores;               // nullptr or [P][Hkv_u][S]
+  uint32_t* flags;             // nullptr or [B]
+  int batch, num_kv_heads, head_dim, table_width, num_pages, keep_stride;
+  int pages_per_unit;          // ceil(keep_stride / S): grid slots per unit
+  bool head_layout, fp8;
+};
+
 // Pool slot of the V block of (page pid, KV head h).  The V block of a
 // (page, head) is not stored at the same slot as its K block: K and V pools
 // are separate allocations, commonly aligned alike, and a wave requests the K
@@ -81,5 +117,7 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head
                             hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 }  // namespace pa

@@ -83,6 +83,16 @@ def lib():
         L.pa_decode_multi_timed.restype = ctypes.c_int
         L.pa_decode_multi_workspace_bytes.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, i32]
         L.pa_decode_multi_workspace_bytes.restype = sz
+        L.pa_decode_scored.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float, i32,
+                                       vp, vp, vp, sz, vp]
+        L.pa_decode_scored.restype = ctypes.c_int
+        L.pa_decode_scored_timed.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float,
+                                             i32, vp, vp, vp, sz, vp, P(vp)]
+        L.pa_decode_scored_timed.restype = ctypes.c_int
+        L.pa_decode_scored_workspace_bytes.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32]
+        L.pa_decode_scored_workspace_bytes.restype = sz
+        L.pa_cache_compact.argtypes = [P(CacheDesc), P(SeqDesc), vp, i32, vp, vp, vp, vp, vp]
+        L.pa_cache_compact.restype = ctypes.c_int
         L.pa_strerror.argtypes = [ctypes.c_int]
         L.pa_strerror.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
@@ -156,6 +166,12 @@ class PagedKVCache:
                 self.k.fill_(0x7F)
                 self.v.fill_(0x7F)
         self.page_tags = None if page_tags is None else _need(page_tags, "page_tags", U32)
+
+    def new_scores(self):
+        """Zeroed eviction scores, fp32 [P][Hkv (SEQ) or 1 (HEAD)][S], laid out like the pages."""
+        heads = self.num_kv_heads if self.layout == "seq" else 1
+        return torch.zeros((self.num_pages, heads, PAGE_SIZE), dtype=torch.float32,
+                           device=self.k.device)
 
     def desc(self):
         return CacheDesc(LAYOUT[self.layout], KV_DTYPE[self.kv_dtype], self.num_pages, PAGE_SIZE,
@@ -238,6 +254,57 @@ def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags
                    num_partitions, out, workspace, events, stream)
 
 
+def decode_scored(cache, q, block_table, lens, softmax_scale, scores, expected_tags=None,
+                  flags=None, num_partitions=0, out=None, workspace=None, events=None, stream=None):
+    """pa_decode_scored: pa_decode, plus each token's attention mass (summed over the
+    query heads of its KV head) added to `scores` (fp32 [P][heads][S], see new_scores)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][D]")
+    heads = cache.num_kv_heads if cache.layout == "seq" else 1
+    _need(scores, "scores", (torch.float32,))
+    if tuple(scores.shape) != (cache.num_pages, heads, PAGE_SIZE):
+        raise ValueError("scores must be [P][%d][%d] fp32" % (heads, PAGE_SIZE))
+    return _decode(cache, q, 1, block_table, lens, softmax_scale, expected_tags, flags,
+                   num_partitions, out, workspace, events, stream, scores=scores)
+
+
+def scored_workspace_bytes(cache, block_table, lens, num_q_heads, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_decode_scored_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                               num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(-1, "pa_decode_scored_workspace_bytes")
+    return n
+
+
+def compact(cache, block_table, lens, keep, n_keep, new_table, scores=None, flags=None,
+            stream=None):
+    """pa_cache_compact: write each unit's kept tokens (keep [B][Hkv][K] positions, n_keep
+    shaped like lens) in order into the pages of new_table (the table's shape)."""
+    sd = _seq(cache, block_table, lens)
+    _need(keep, "keep", I32)
+    _need(n_keep, "n_keep", I32)
+    _need(new_table, "new_table", I32)
+    B = block_table.shape[0]
+    if keep.dim() != 3 or keep.shape[0] != B or keep.shape[1] != cache.num_kv_heads:
+        raise ValueError("keep must be [B][Hkv][K]")
+    if tuple(n_keep.shape) != tuple(lens.shape) or tuple(new_table.shape) != tuple(block_table.shape):
+        raise ValueError("n_keep must have lens' shape and new_table the table's")
+    if scores is not None:
+        _need(scores, "scores", (torch.float32,))
+    if flags is not None:
+        _need(flags, "flags", U32)
+        if flags.numel() != B:
+            raise ValueError("flags must hold B words")
+    cd = cache.desc()
+    rc = lib().pa_cache_compact(ctypes.byref(cd), ctypes.byref(sd), _ptr(keep), keep.shape[2],
+                                _ptr(n_keep), _ptr(new_table), _ptr(scores), _ptr(flags),
+                                _stream(stream))
+    if rc != 0:
+        raise PAError(rc, "pa_cache_compact")
+
+
 def decode_multi(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
                  num_partitions=0, out=None, workspace=None, events=None, stream=None):
     """pa_decode_multi: q [B][T][Hq][D] BF16 (T draft tokens, the last T of each unit,
@@ -259,7 +326,7 @@ def multi_workspace_bytes(cache, block_table, lens, num_q_heads, q_len, num_part
 
 
 def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, flags,
-            num_partitions, out, workspace, events, stream):
+            num_partitions, out, workspace, events, stream, scores=None):
     sd = _seq(cache, block_table, lens, expected_tags)
     _need(q, "q", BF16)
     if q.shape[0] != block_table.shape[0] or q.shape[-1] != cache.head_dim:
@@ -276,7 +343,10 @@ def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, fl
     cd = cache.desc()
     Hq = q.shape[-2]
     L = lib()
-    if q_len == 1:
+    if scores is not None:
+        need = L.pa_decode_scored_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq,
+                                                  num_partitions)
+    elif q_len == 1:
         need = L.pa_decode_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, num_partitions)
     else:
         need = L.pa_decode_multi_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, q_len,
@@ -290,7 +360,17 @@ def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, fl
     args = (ctypes.byref(cd), ctypes.byref(sd), Hq)
     tail = (_ptr(q), _ptr(out), float(softmax_scale), num_partitions, _ptr(flags), ws_ptr,
             ws_bytes, _stream(stream))
-    if events is None:
+    if scores is not None:
+        tail_s = tail[:5] + (_ptr(scores),) + tail[5:]
+        if events is None:
+            rc = L.pa_decode_scored(*args, *tail_s)
+        else:
+            for e in events:
+                if e is not None and not e.cuda_event:
+                    e.record()
+            ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+            rc = L.pa_decode_scored_timed(*args, *tail_s, ev)
+    elif events is None:
         if q_len == 1:
             rc = L.pa_decode(*args, *tail)
         else:

@@ -26,6 +26,11 @@
  *             (page, tag) pairs each request expects; a separate batch
  *             validation checks them before decode reads the cache; a request
  *             that fails is aborted; with checking off the tracker is a no-op.
+ *   [evict]   "Making Workers AI faster and more efficient", section "KV cache
+ *             compression goes open source": eviction drops the KV entries
+ *             with the least accumulated past attention (a least-frequently-
+ *             used policy); with a per-head block table every head can keep a
+ *             different number of tokens.
  *
  * Conventions for every entry point:
  *   - All buffer pointers are DEVICE pointers unless stated otherwise; the
@@ -93,7 +98,8 @@ enum {
 enum {
   PA_FLAG_TAG_MISMATCH = 1u, /* expected tag != page tag for a page it would read */
   PA_FLAG_PAGE_OOB = 2u,     /* a page id it would read or write is outside [0, num_pages) */
-  PA_FLAG_LEN_OVERFLOW = 4u  /* a length exceeds table_width * page_size */
+  PA_FLAG_LEN_OVERFLOW = 4u, /* a length exceeds table_width * page_size */
+  PA_FLAG_KEEP_INVALID = 8u  /* pa_cache_compact: a keep position outside [0, len) */
 };
 
 /* The physical cache ([paging], [table], [fp8], [tags]). */
@@ -241,6 +247,76 @@ int pa_decode_multi_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
 size_t pa_decode_multi_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
                                        int32_t num_q_heads, int32_t q_len,
                                        int32_t num_partitions);
+
+/*
+ * Decode that also updates eviction scores ([evict]).
+ *
+ * Everything pa_decode does and produces (q_len 1), bit for bit, plus: for
+ * every unit that is not flagged, each of its lens[u] tokens gets the
+ * softmax weight the step put on it, summed over the Hq / Hkv query heads of
+ * the unit's KV head, added to its score:
+ *   scores: device fp32, laid out like the pages -- SEQ [num_pages][Hkv][16],
+ *           HEAD [num_pages][16]; entry (page, head, slot) is the token that
+ *           K/V slot holds, so scores move with their pages.  Read and written
+ *           in place (the caller zeroes a page's scores when it reallocates
+ *           it).  Flagged sequences, slots past lens[u] and pages outside the
+ *           pool (unchecked ids) are not touched.
+ * The weights are those of the full softmax over the unit's tokens, computed
+ * from the same fp32 scores the attention used, normalised with the row's
+ * final max and sum after the partition merge.
+ * Workspace: pa_decode_scored_workspace_bytes(...) bytes, never 0 (the
+ * scores of every page are staged there: B * Hkv * table_width * (Hq/Hkv) *
+ * 64 bytes, plus the partials of pa_decode and B * Hq * 8 bytes).
+ * Data races: two concurrent calls on the same scores array race.
+ */
+int pa_decode_scored(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+                     const uint16_t *q, uint16_t *out, float softmax_scale,
+                     int32_t num_partitions, uint32_t *flags, float *scores, void *workspace,
+                     size_t workspace_bytes, pa_stream_t stream);
+
+/* pa_decode_scored with the timing events of pa_decode_timed (events[3] is
+ * recorded after the score update). */
+int pa_decode_scored_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                           int32_t num_q_heads, const uint16_t *q, uint16_t *out,
+                           float softmax_scale, int32_t num_partitions, uint32_t *flags,
+                           float *scores, void *workspace, size_t workspace_bytes,
+                           pa_stream_t stream, pa_event_t const events[4]);
+
+/* Workspace bytes of pa_decode_scored; (size_t)-1 for invalid arguments. */
+size_t pa_decode_scored_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                                        int32_t num_q_heads, int32_t num_partitions);
+
+/*
+ * Compaction after eviction ([evict]): rewrite the tokens each unit keeps, in
+ * the given order, from position 0 into the pages of a new table.
+ *   seq:       the OLD table and lengths (seq->expected_tags is ignored).
+ *   keep:      device int32 [B][Hkv][keep_stride]; keep[b][h][i] is the old
+ *              position (0 <= p < lens) of the i-th token unit (b, h) keeps.
+ *   n_keep:    device int32, lens' shape (SEQ [B]: every head of a sequence
+ *              keeps the same number of tokens, as the SEQ layout has one
+ *              length per sequence; HEAD [B][Hkv]: per head).  n_keep <=
+ *              keep_stride and <= table_width * 16.
+ *   new_table: device int32, the old table's shape; entries 0 ..
+ *              ceil(n_keep / 16) - 1 of a row name the destination pages.
+ *              They must not be pages this call reads (the caller allocates
+ *              fresh pages and frees the old ones afterwards).
+ *   scores:    NULL, or the eviction scores (see pa_decode_scored): each
+ *              kept token's score moves with it.
+ *   flags:     NULL or device uint32 [B], overwritten: PA_FLAG_PAGE_OOB for an
+ *              old or new page id out of range, PA_FLAG_LEN_OVERFLOW for a
+ *              length or count above the table or a count above keep_stride,
+ *              PA_FLAG_KEEP_INVALID for a position outside [0, lens).  Such
+ *              tokens are not written.
+ * BF16 tokens are copied bit for bit.  FP8 tokens are decoded under their old
+ * page scale, x = fl32(decode(c) * s_old), and re-quantised under the new
+ * page's scale s = fl32(amax / 448) over the x the page receives, codes
+ * RNE_e4m3(saturate(fl32(x / s))) -- the rule of an append into fresh pages.
+ * Slots past n_keep in a unit's last new page are left as they were.  The
+ * caller then uses new_table with lengths n_keep.
+ */
+int pa_cache_compact(const pa_cache_desc *cache, const pa_seq_desc *seq, const int32_t *keep,
+                     int32_t keep_stride, const int32_t *n_keep, const int32_t *new_table,
+                     float *scores, uint32_t *flags, pa_stream_t stream);
 
 /* Static text for a PA_* return code. */
 const char *pa_strerror(int code);

@@ -55,16 +55,17 @@ def dense_tokens(kv_b, layout, h):
     return K, V
 
 
-def oracle_sequence(w, b):
+def oracle_sequence(w, b, with_mass=False):
     """Oracle result of sequence b alone, on a compact local pool.
 
     The sequence's pages are renumbered 0..n-1 (the result does not depend on
     physical page ids: page-permutation invariance is pinned separately).
     Returns dict(pages=global page ids [n], k, v = local logical pools [n][H][S][D],
     k_scale, v_scale = [n][H] or None, out = fp64 [Hq][D], or [T][Hq][D] for a
-    multi-query workload (unflagged result)).
+    multi-query workload (unflagged result)); with_mass adds mass = {h: the
+    step's attention mass per token [L]} (decode workloads).
     """
-    from oracle import oracle_decode, oracle_decode_multi
+    from oracle import oracle_attention_mass, oracle_decode, oracle_decode_multi
 
     rows = w.block_table[b:b + 1]
     lens = w.lens[b:b + 1]
@@ -86,9 +87,13 @@ def oracle_sequence(w, b):
         out = oracle_decode(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
     else:
         out = oracle_decode_multi(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
-    return dict(pages=pages, k=cache.k[:len(pages)], v=cache.v[:len(pages)],
-                k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
-                v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)], out=out)
+    r = dict(pages=pages, k=cache.k[:len(pages)], v=cache.v[:len(pages)],
+             k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
+             v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)], out=out)
+    if with_mass:
+        m = oracle_attention_mass(cache, w.q[b:b + 1], local, lens, w.sigma)
+        r["mass"] = {h: m[(0, h)] for (_, h) in m}
+    return r
 
 
 class _SubWorkload:
@@ -106,7 +111,7 @@ class _SubWorkload:
         return self._w.seq_kv(self._b)
 
 
-def oracle_sequences_parallel(w, seqs, workers=None):
+def oracle_sequences_parallel(w, seqs, workers=None, with_mass=False):
     """oracle_sequence for several sequences in a process pool."""
     import multiprocessing
     import os
@@ -114,7 +119,8 @@ def oracle_sequences_parallel(w, seqs, workers=None):
 
     workers = workers or max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
     if workers == 1:
-        return {b: oracle_sequence(w, b) for b in seqs}
+        return {b: oracle_sequence(w, b, with_mass) for b in seqs}
     # spawn: a forked child of a process with live OpenMP/torch thread pools can deadlock
     with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
-        return dict(zip(seqs, ex.map(oracle_sequence, [w] * len(seqs), seqs)))
+        return dict(zip(seqs, ex.map(oracle_sequence, [w] * len(seqs), seqs,
+                                     [with_mass] * len(seqs))))

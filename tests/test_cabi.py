@@ -27,7 +27,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror",
-              "pa_decode_multi", "pa_decode_multi_workspace_bytes"):
+              "pa_decode_multi", "pa_decode_multi_workspace_bytes", "pa_decode_scored",
+              "pa_cache_compact"):
         assert n in names
 
 
@@ -162,6 +163,44 @@ def test_decode_multi_rejects_bad_arguments():
     assert wsm(8 * 16, 8, 2) == ctypes.c_size_t(-1).value
     need = wsm(32, 4, 4)
     assert _decode_multi(c, s, parts=4, ws=FAKE, ws_bytes=need - 1) == -3
+
+
+def test_decode_scored_arguments_and_workspace():
+    L = pa.lib()
+    c, s = _cache(), _seq()
+    sc = lambda scores=FAKE, ws=None, ws_bytes=0, parts=0, hq=32: L.pa_decode_scored(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(s), hq, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 0.088,
+        parts, None, ctypes.c_void_p(scores) if scores else None,
+        ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert sc(scores=0) == -1
+    assert sc(scores=FAKE + 2) == -1
+    need1 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 1)
+    # page scores [B*Hkv][W][G][16] fp32 + rows' (max, sum) [B][Hq][2]; no partials at Pn = 1
+    assert need1 == 4 * 8 * 64 * 4 * 16 * 4 + 4 * 32 * 2 * 4
+    need4 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
+    assert need4 == need1 + L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
+    assert sc(ws=None) == -3                                  # always needs a workspace
+    assert sc(ws=FAKE, ws_bytes=need1 - 1, parts=1) == -3
+    assert sc(hq=8 * 17) == -2
+
+
+def test_compact_rejects_bad_arguments():
+    L = pa.lib()
+    c, s = _cache(), _seq()
+    cp = lambda keep=FAKE, stride=16, n_keep=FAKE, nt=FAKE, scores=None, fl=None, cc=c: (  # noqa: E731
+        L.pa_cache_compact(ctypes.byref(cc), ctypes.byref(s), ctypes.c_void_p(keep) if keep else None,
+                           stride, ctypes.c_void_p(n_keep) if n_keep else None,
+                           ctypes.c_void_p(nt) if nt else None,
+                           ctypes.c_void_p(scores) if scores else None,
+                           ctypes.c_void_p(fl) if fl else None, None))
+    assert cp(keep=0) == -1
+    assert cp(stride=0) == -1
+    assert cp(n_keep=0) == -1
+    assert cp(nt=0) == -1
+    assert cp(keep=FAKE + 2) == -1
+    assert cp(scores=FAKE + 1) == -1
+    assert cp(fl=FAKE + 2) == -1
+    assert cp(cc=_cache(head_dim=80)) == -2
 
 
 def test_append_rejects_bad_arguments():
