@@ -26,6 +26,10 @@ pa_decode_multi attends them causally; tokens/s then counts verified tokens.
 --scored makes the decode a scored decode (eviction scores updated in place).
 --compact F times pa_cache_compact keeping a fraction F of every unit's
 tokens (random positions) into spare pages, and reports its GB/s instead.
+--prefill C times a chunked-prefill step (append of a C-token chunk, then
+pa_prefill) on a Llama-3.1-8B-shaped BF16 layer: 4 sequences whose cached
+prefixes are 0, 2K, 8K and 30K tokens; it reports TFLOP/s against the MFMA
+bf16 peak.
 """
 import argparse
 import hashlib
@@ -39,6 +43,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_PREFIXES = (0, 2048, 8192, 30720)
+
+
+def prefill_flops(w):
+    """Multiply-adds of the chunk's attention, x2: query t of a unit with L tokens
+    sees L - C + t + 1 of them, and costs 2*D for q.k plus 2*D for p*v per token."""
+    import numpy as np
+
+    C = w.q_len
+    L = w.lens.astype(np.int64).reshape(-1)
+    per_unit = [int((L_u - C) * C + C * (C + 1) // 2) for L_u in L]   # sum over t of visible tokens
+    heads_per_unit = w.Hq if w.layout == "seq" else w.G
+    return 4 * w.D * heads_per_unit * sum(per_unit)
 
 
 def log(msg):
@@ -264,6 +282,8 @@ def main():
     ap.add_argument("--scored", action="store_true", help="scored decode (eviction scores)")
     ap.add_argument("--compact", type=float, default=0.0,
                     help="time compaction to this fraction of the tokens instead")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="time a chunked-prefill step with this chunk length instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
     args = ap.parse_args()
@@ -293,11 +313,16 @@ def main():
         return
     if args.compact > 0:
         return bench_compaction(args)
-    w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len)
+    if args.prefill > 0:
+        C = args.prefill
+        w = make_workload(2, batch=len(PREFILL_PREFIXES), stale_frac=0.0, q_len=C,
+                          lens=np.array(PREFILL_PREFIXES) + C, table_width=2048)
+    else:
+        w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len)
     # split-K 8 is the decode workload's own setting; multi-query steps take the
     # library's choice (whole grid resident: 4 on the 70B-shaped workload)
-    parts = args.partitions if args.partitions >= 0 else (8 if args.config == 5 and args.q_len == 1
-                                                          else 0)
+    parts = args.partitions if args.partitions >= 0 else (
+        8 if args.config == 5 and args.q_len == 1 and args.prefill == 0 else 0)
     check = not args.no_check
     T = w.q_len
     log("workload %d %s: B=%d Hq=%d Hkv=%d D=%d kv=%s layout=%s tokens=%d q_len=%d" % (
@@ -311,6 +336,9 @@ def main():
     if args.scored:
         ws_bytes = pa.scored_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, parts)
         scores = dw.cache.new_scores()
+    elif args.prefill > 0:
+        ws_bytes = pa.prefill_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
+        n_parts = pa.prefill_num_partitions(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
     else:
         ws_bytes = pa.multi_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -366,7 +394,7 @@ def main():
             100 * attn_gbs / HBM_PEAK_GBS))
 
     graph = None
-    if not args.no_graph and not args.scored:
+    if not args.no_graph and not args.scored and args.prefill == 0:
         g = pa.DecodeStepGraph(dw.cache, dw.block_table, dw.lens_old, dw.n_step, dw.k_step,
                                dw.v_step, dw.q, dw.lens, w.sigma,
                                expected_tags=dw.expected_tags if check else None,
@@ -391,6 +419,35 @@ def main():
         del g
 
     traffic = traffic_from_profile(w.name if T == 1 else "%s-t%d" % (w.name, T), None)
+    if args.prefill > 0:
+        fl = prefill_flops(w)
+        tflops = fl / (t_attn.mean() * 1e-3) / 1e12
+        log("prefill: %.3g GFLOP per step; attention kernel %.1f us = %.0f TFLOP/s (%.1f%% of "
+            "the %d TFLOP/s bf16 MFMA peak)" % (fl / 1e9, t_attn.mean() * 1e3, tflops,
+                                                 100 * tflops / MFMA_BF16_PEAK_TFLOPS,
+                                                 MFMA_BF16_PEAK_TFLOPS))
+    if args.prefill > 0:
+        step_tflops = fl / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "chunked prefill attention over the paged cache: achieved TFLOP/s",
+            "value": round(step_tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "llama8b-prefill: B=4, Hq=32, Hkv=8, D=128, page 16, BF16 KV, "
+                                   "SEQ layout, cached prefixes %s, chunk %d, %d partitions, tag "
+                                   "check %s" % (list(PREFILL_PREFIXES), T, n_parts,
+                                                 "on" if check else "off"),
+                       "global_batch": w.B, "chunk_tokens": T},
+            "flops_per_step": fl,
+            "kernels_us": {"append": round(t_append.mean() * 1e3, 2),
+                           "validate": round(t_val.mean() * 1e3, 2),
+                           "attention": round(t_attn.mean() * 1e3, 2),
+                           "reduce": round(t_red.mean() * 1e3, 2)},
+            "roofline": {"bound": "mfma", "kernel": "attention_kernel", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+            "cpu_baseline": None}), flush=True)
+        return
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0: eviction scores and compaction
+constexpr int kVersion = 400;  // 0.4.0: chunked prefill
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -123,22 +123,62 @@ size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, i
   return workspace_layout(c, s, hq, q_len, parts, scored).total;
 }
 
+// Chunked prefill: a unit's G * T query columns go in blocks of 64, one wave
+// per block, so there are far more waves than units; split-K is only needed
+// when the grid would otherwise be small.
+int prefill_col_blocks(const pa_cache_desc* c, int32_t hq, int32_t q_len) {
+  const int64_t cols = (int64_t)(hq / c->num_kv_heads) * q_len;
+  return (int)((cols + pa::kMaxCols - 1) / pa::kMaxCols);
+}
+
+void choose_prefill_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
+                               int32_t q_len, int32_t req, int* chunk_pages, int* num_parts) {
+  const int W = s->table_width;
+  int parts = req;
+  if (req <= 0) {
+    const int64_t waves = (int64_t)s->batch * c->num_kv_heads * prefill_col_blocks(c, hq, q_len);
+    int64_t p = (kTargetWaves + waves - 1) / waves;
+    const int64_t pmax = (W + 31) / 32;               // partitions of at least 32 pages
+    parts = (int)(p < 1 ? 1 : (p > pmax ? pmax : p));
+  }
+  int cp = (W + parts - 1) / parts;
+  if (cp > W) cp = W;
+  if (cp < 1) cp = 1;
+  *chunk_pages = cp;
+  *num_parts = (W + cp - 1) / cp;
+}
+
+int check_prefill(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len) {
+  if (hq <= 0 || hq % c->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (hq / c->num_kv_heads > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (q_len < 1 || (int64_t)q_len > (int64_t)s->table_width * pa::kPageSize) return PA_ERR_INVALID_ARG;
+  if ((int64_t)s->batch * q_len * hq > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
                 int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
                 int32_t num_partitions, uint32_t* flags, void* workspace, size_t workspace_bytes,
-                hipStream_t stream, pa_event_t const* events, float* scores = nullptr) {
+                hipStream_t stream, pa_event_t const* events, float* scores = nullptr,
+                bool prefill = false) {
   int rc;
   if ((rc = check_cache(cache)) != PA_OK) return rc;
   if ((rc = check_seq(seq)) != PA_OK) return rc;
-  if ((rc = check_heads(cache, num_q_heads, q_len)) != PA_OK) return rc;
+  if (prefill) {
+    if ((rc = check_prefill(cache, seq, num_q_heads, q_len)) != PA_OK) return rc;
+  } else if ((rc = check_heads(cache, num_q_heads, q_len)) != PA_OK) {
+    return rc;
+  }
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return PA_ERR_INVALID_ARG;
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
   if (seq->expected_tags && (!flags || !cache->page_tags)) return PA_ERR_INVALID_ARG;
   if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
   if (scores && (q_len != 1 || !aligned(scores, 4))) return PA_ERR_INVALID_ARG;
-  int chunk_pages, parts, ppw;
-  choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
+  int chunk_pages, parts, ppw = 1;
+  if (prefill) choose_prefill_partitions(cache, seq, num_q_heads, q_len, num_partitions,
+                                         &chunk_pages, &parts);
+  else choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
   const WorkspaceLayout wl =
       workspace_layout(cache, seq, num_q_heads, q_len, parts, scores != nullptr);
   const size_t need = wl.total;
@@ -192,6 +232,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.q_len = q_len;
+  a.col_blocks = prefill ? prefill_col_blocks(cache, num_q_heads, q_len) : 1;
   a.table_width = seq->table_width;
   a.num_pages = cache->num_pages;
   a.chunk_pages = chunk_pages;
@@ -199,7 +240,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.parts_per_wave = ppw;
   // XCD-aware workgroup order needs whole groups of 4 heads; the SEQ layout
   // gains most from it (the heads of a page share its blocks and scales).
-  a.xcd_order = (cache->num_kv_heads % pa::kWaves == 0) ? 1 : 0;
+  a.xcd_order = (cache->num_kv_heads % pa::kWaves == 0 && a.col_blocks == 1) ? 1 : 0;
 #ifdef PA_NO_XCD_ORDER
   a.xcd_order = 0;
 #endif
@@ -401,6 +442,49 @@ PA_API int pa_cache_compact(const pa_cache_desc* cache, const pa_seq_desc* seq,
   if (pa::launch_compact(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+PA_API size_t pa_prefill_workspace_bytes(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                         int32_t num_q_heads, int32_t chunk_len,
+                                         int32_t num_partitions) {
+  if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
+      check_prefill(cache, seq, num_q_heads, chunk_len) != PA_OK || num_partitions < 0)
+    return (size_t)-1;
+  int cp, parts;
+  choose_prefill_partitions(cache, seq, num_q_heads, chunk_len, num_partitions, &cp, &parts);
+  return workspace_for(cache, seq, num_q_heads, chunk_len, parts);
+}
+
+PA_API int pa_prefill_num_partitions(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                     int32_t num_q_heads, int32_t chunk_len,
+                                     int32_t num_partitions) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  if ((rc = check_prefill(cache, seq, num_q_heads, chunk_len)) != PA_OK) return rc;
+  if (num_partitions < 0) return PA_ERR_INVALID_ARG;
+  int cp, parts;
+  choose_prefill_partitions(cache, seq, num_q_heads, chunk_len, num_partitions, &cp, &parts);
+  return parts;
+}
+
+PA_API int pa_prefill(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
+                      int32_t chunk_len, const uint16_t* q, uint16_t* out, float softmax_scale,
+                      int32_t num_partitions, uint32_t* flags, void* workspace,
+                      size_t workspace_bytes, pa_stream_t stream) {
+  return decode_impl(cache, seq, num_q_heads, chunk_len, q, out, softmax_scale, num_partitions,
+                     flags, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                     nullptr, nullptr, true);
+}
+
+PA_API int pa_prefill_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                            int32_t num_q_heads, int32_t chunk_len, const uint16_t* q,
+                            uint16_t* out, float softmax_scale, int32_t num_partitions,
+                            uint32_t* flags, void* workspace, size_t workspace_bytes,
+                            pa_stream_t stream, pa_event_t const events[4]) {
+  return decode_impl(cache, seq, num_q_heads, chunk_len, q, out, softmax_scale, num_partitions,
+                     flags, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                     events, nullptr, true);
 }
 
 PA_API int pa_decode_multi(const pa_cache_desc* cache, const pa_seq_desc* seq,

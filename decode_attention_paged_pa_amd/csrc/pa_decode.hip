@@ -181,10 +181,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   const int T = CAUSAL ? a.q_len : 1;
   const int C = G * T;                         // query columns of the unit
+  // Long chunks (prefill) split a unit's columns into blocks of 16 * NQ, one
+  // wave per block; a block reads only the pages its last column can see.
+  const int cblocks = a.col_blocks;
   // readfirstlane: the wave index is uniform, and saying so keeps every
   // per-page index, bound and branch in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b, h, g;  // sequence, KV head, partition group of this wave
+  int b, h, g, cb = 0;  // sequence, KV head, partition group, column block of this wave
   if (a.xcd_order) {
     // Workgroups are dealt to the 8 XCDs in turn (id % 8).  A workgroup holds
     // 4 heads of one (sequence, partition group) pair, and the Hkv/4
@@ -204,12 +207,16 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     h = hg * kWaves + wave;
   } else {
     const int item = blockIdx.x * kWaves + wave;
-    if (item >= a.batch * Hkv * groups) return;
-    const int unit = item / groups;
-    g = item - unit * groups;
+    if (item >= a.batch * Hkv * cblocks * groups) return;
+    const int rest = item / groups;
+    g = item - rest * groups;
+    const int unit = rest / cblocks;
+    cb = rest - unit * cblocks;
     b = unit / Hkv;
     h = unit - b * Hkv;
   }
+  const int cbase = cb * 16 * NQ;              // first column of this wave's block
+  const int cend = min(cbase + 16 * NQ, C);
   const int unit = b * Hkv + h;
   const int part0 = g * ppw;  // first partition of this wave
   const int row = HEAD ? unit : b;
@@ -220,7 +227,11 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int cap = a.table_width * kPageSize;
   int L = a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int npages = (L + kPageSize - 1) / kPageSize;
+  int npages = (L + kPageSize - 1) / kPageSize;
+  if (CAUSAL) {  // the block's last column sees L - T + t_last + 1 tokens
+    const int seen = L - T + (cend - 1) / G + 1;
+    npages = seen > 0 ? min(npages, (seen + kPageSize - 1) / kPageSize) : 0;
+  }
   const int p0 = part0 * a.chunk_pages;
   const int p1 = min(min(part0 + ppw, Pn) * a.chunk_pages, npages);
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
@@ -231,7 +242,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   };
   if (flagged || p0 >= p1) {
     if (Pn == 1) {  // no reduce follows: this wave owns the output rows
-      for (int i = lane; i < C * D; i += 64) a.out[col_row(i / D) * D + i % D] = 0;
+      for (int i = lane; i < (cend - cbase) * D; i += 64)
+        a.out[col_row(cbase + i / D) * D + i % D] = 0;
     }
     return;
   }
@@ -244,8 +256,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   int lim[NQ];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
-    const int cc = 16 * nq + c;
-    const bool ok = cc < C;
+    const int cc = cbase + 16 * nq + c;
+    const bool ok = cc < cend;
     const uint16_t* qrow = a.q + col_row(ok ? cc : 0) * D;
     lim[nq] = CAUSAL ? L - T + (ok ? cc / G : 0) + 1 : L;
 #pragma unroll
@@ -260,7 +272,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   }
   // first token that some column cannot see: pages at or past it need masks
-  const int vis_min = CAUSAL ? L - T + 1 : L;
+  const int vis_min = CAUSAL ? L - T + cbase / G + 1 : L;
 
   f32x4 o[NQ][NT];
   float m_run[NQ], l_acc[NQ];
@@ -460,8 +472,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const float l_tot = col_sum(l_acc[nq]);
-      const int cc = 16 * nq + c;
-      if (cc < C) {
+      const int cc = cbase + 16 * nq + c;
+      if (cc < cend) {
         const size_t qrow = col_row(cc);
         if (Pn == 1) {
           if constexpr (SCORE) {
@@ -640,7 +652,7 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const unsigned pairs = (unsigned)a.batch * groups;
     grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
   } else {
-    const unsigned items = (unsigned)a.batch * a.num_kv_heads * groups;
+    const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.col_blocks * groups;
     grid = (items + kWaves - 1) / kWaves;
   }
   hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL, SCORE>), dim3(grid),

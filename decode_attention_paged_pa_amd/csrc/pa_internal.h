@@ -27,6 +27,7 @@ struct AttnArgs {
   float* part_ml;            // [B][q_len][Hq][Pn][2] running max (log2 domain) and sum
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int q_len;                 // query tokens per sequence (1: decode; > 1: causal drafts)
+  int col_blocks;            // blocks of 64 query columns per unit (prefill chunks); else 1
   float* logits;             // scored decode: [units][W][G][16] log2-domain scores, else nullptr
   float* row_ml;             // scored decode: [B][Hq][2] final max (log2) and sum per row
   int chunk_pages, num_parts;

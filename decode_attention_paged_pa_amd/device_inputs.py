@@ -35,7 +35,8 @@ class DeviceWorkload:
                   self.v_step, flags=flags)
 
     def decode(self, check=True, num_partitions=0, out=None, workspace=None, events=None):
-        run = pa.decode if self.w.q_len == 1 else pa.decode_multi
+        run = pa.decode if self.w.q_len == 1 else (pa.decode_multi if self.w.q_len <= 8
+                                                   else pa.prefill)
         return run(self.cache, self.q, self.block_table, self.lens, self.w.sigma,
                    expected_tags=self.expected_tags if check else None,
                    flags=self.flags if check else None, num_partitions=num_partitions,

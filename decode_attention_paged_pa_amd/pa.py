@@ -93,6 +93,16 @@ def lib():
         L.pa_decode_scored_workspace_bytes.restype = sz
         L.pa_cache_compact.argtypes = [P(CacheDesc), P(SeqDesc), vp, i32, vp, vp, vp, vp, vp]
         L.pa_cache_compact.restype = ctypes.c_int
+        L.pa_prefill.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, vp, vp, ctypes.c_float, i32,
+                                 vp, vp, sz, vp]
+        L.pa_prefill.restype = ctypes.c_int
+        L.pa_prefill_timed.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, vp, vp, ctypes.c_float,
+                                       i32, vp, vp, sz, vp, P(vp)]
+        L.pa_prefill_timed.restype = ctypes.c_int
+        L.pa_prefill_workspace_bytes.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, i32]
+        L.pa_prefill_workspace_bytes.restype = sz
+        L.pa_prefill_num_partitions.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, i32]
+        L.pa_prefill_num_partitions.restype = ctypes.c_int
         L.pa_strerror.argtypes = [ctypes.c_int]
         L.pa_strerror.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
@@ -315,6 +325,36 @@ def decode_multi(cache, q, block_table, lens, softmax_scale, expected_tags=None,
                    num_partitions, out, workspace, events, stream)
 
 
+def prefill(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
+            num_partitions=0, out=None, workspace=None, events=None, stream=None):
+    """pa_prefill: q [B][C][Hq][D] BF16 (a chunk of C prompt tokens, the last C of each unit,
+    already appended) -> out [B][C][Hq][D] BF16; token t sees tokens 0 .. L - C + t."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][C][Hq][D]")
+    return _decode(cache, q, q.shape[1], block_table, lens, softmax_scale, expected_tags, flags,
+                   num_partitions, out, workspace, events, stream, prefill=True)
+
+
+def prefill_workspace_bytes(cache, block_table, lens, num_q_heads, chunk_len, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_prefill_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                         chunk_len, num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(-1, "pa_prefill_workspace_bytes")
+    return n
+
+
+def prefill_num_partitions(cache, block_table, lens, num_q_heads, chunk_len, num_partitions=0):
+    sd = _seq(cache, block_table, lens)
+    cd = cache.desc()
+    n = lib().pa_prefill_num_partitions(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,
+                                        chunk_len, num_partitions)
+    if n < 0:
+        raise PAError(n, "pa_prefill_num_partitions")
+    return n
+
+
 def multi_workspace_bytes(cache, block_table, lens, num_q_heads, q_len, num_partitions=0):
     sd = _seq(cache, block_table, lens)
     cd = cache.desc()
@@ -326,7 +366,7 @@ def multi_workspace_bytes(cache, block_table, lens, num_q_heads, q_len, num_part
 
 
 def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, flags,
-            num_partitions, out, workspace, events, stream, scores=None):
+            num_partitions, out, workspace, events, stream, scores=None, prefill=False):
     sd = _seq(cache, block_table, lens, expected_tags)
     _need(q, "q", BF16)
     if q.shape[0] != block_table.shape[0] or q.shape[-1] != cache.head_dim:
@@ -343,7 +383,10 @@ def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, fl
     cd = cache.desc()
     Hq = q.shape[-2]
     L = lib()
-    if scores is not None:
+    if prefill:
+        need = L.pa_prefill_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq, q_len,
+                                            num_partitions)
+    elif scores is not None:
         need = L.pa_decode_scored_workspace_bytes(ctypes.byref(cd), ctypes.byref(sd), Hq,
                                                   num_partitions)
     elif q_len == 1:
@@ -360,7 +403,16 @@ def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, fl
     args = (ctypes.byref(cd), ctypes.byref(sd), Hq)
     tail = (_ptr(q), _ptr(out), float(softmax_scale), num_partitions, _ptr(flags), ws_ptr,
             ws_bytes, _stream(stream))
-    if scores is not None:
+    if prefill:
+        if events is None:
+            rc = L.pa_prefill(*args, q_len, *tail)
+        else:
+            for e in events:
+                if e is not None and not e.cuda_event:
+                    e.record()
+            ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+            rc = L.pa_prefill_timed(*args, q_len, *tail, ev)
+    elif scores is not None:
         tail_s = tail[:5] + (_ptr(scores),) + tail[5:]
         if events is None:
             rc = L.pa_decode_scored(*args, *tail_s)
@@ -413,6 +465,9 @@ class DecodeStepGraph:
         self.out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         if q.dim() == 3:
             need = workspace_bytes(cache, block_table, lens, q.shape[1], num_partitions)
+        elif q.shape[1] > 8:
+            need = prefill_workspace_bytes(cache, block_table, lens, q.shape[2], q.shape[1],
+                                           num_partitions)
         else:
             need = multi_workspace_bytes(cache, block_table, lens, q.shape[2], q.shape[1],
                                          num_partitions)
@@ -430,7 +485,7 @@ class DecodeStepGraph:
     def _step(self):
         (cache, bt, lens_old, n_new, k_new, v_new, q, lens, scale, exp, flags, parts) = self.args
         append(cache, bt, lens_old, n_new, k_new, v_new)
-        run = decode if q.dim() == 3 else decode_multi
+        run = decode if q.dim() == 3 else (decode_multi if q.shape[1] <= 8 else prefill)
         run(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
             out=self.out, workspace=self.workspace)
 

@@ -125,11 +125,12 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     batch / lens / table_width override the workload's own sizes for reduced
     parity cases; stale_frac overrides the fraction of stale expected tags
     (workload 3 defaults to 0.01, the others to 0); q_len > 1 makes the step
-    a multi-query (speculative verification) step of q_len draft tokens;
+    a multi-query step of q_len query tokens (speculative verification: up to
+    8 drafts; chunked prefill: a chunk of q_len prompt tokens);
     heads = (Hq, Hkv) overrides the head counts (edge cases of the grouping).
     """
-    if not 1 <= int(q_len) <= 8:
-        raise ValueError("q_len must be in 1..8")
+    if int(q_len) < 1:
+        raise ValueError("q_len must be at least 1")
     seed = cfg_id if seed is None else seed
     rng = np.random.default_rng(seed)
     spec = {

@@ -6,7 +6,10 @@
  *     block table, quantising to FP8 e4m3 with per-(page, KV head) scales
  *     when the cache is FP8;
  *   - pa_decode checks the page tags a request expects, then runs grouped-
- *     query attention of one query token per sequence over every cached token.
+ *     query attention of one query token per sequence over every cached token;
+ * and around it: pa_decode_multi (speculative verification of up to 8 draft
+ * tokens), pa_prefill (chunked prefill), pa_decode_scored (eviction scores)
+ * and pa_cache_compact (compaction after eviction).
  *
  * Sources (web pages; the citations name the page title and the passage):
  *   [paging]  "How we built the most efficient inference engine for
@@ -240,6 +243,40 @@ int pa_decode_multi_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
                           float softmax_scale, int32_t num_partitions, uint32_t *flags,
                           void *workspace, size_t workspace_bytes, pa_stream_t stream,
                           pa_event_t const events[4]);
+
+/*
+ * Chunked prefill over the paged cache ([paging]: prefill processes the
+ * prompt tokens in parallel; the batcher mixes decode with chunks of prefill
+ * tokens -- "How we built the most efficient inference engine for
+ * Cloudflare's network", section "Batching to feed the Tensor Cores").
+ *
+ * The same computation as pa_decode_multi with q_len = chunk_len, for chunks
+ * of any length up to table_width * 16: the chunk's tokens are the last
+ * chunk_len tokens of every unit (appended before the call); token t sees
+ * tokens 0 .. lens[u] - chunk_len + t (the cached prefix and the chunk up to
+ * itself).  q, out: device BF16 [B][chunk_len][Hq][D].
+ * The query columns (heads x chunk tokens) of a unit go to waves in blocks of
+ * 64; num_partitions (0 = automatic) splits the prefix only when the grid
+ * would otherwise be small.  Workspace: pa_prefill_workspace_bytes(...).
+ */
+int pa_prefill(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+               int32_t chunk_len, const uint16_t *q, uint16_t *out, float softmax_scale,
+               int32_t num_partitions, uint32_t *flags, void *workspace, size_t workspace_bytes,
+               pa_stream_t stream);
+
+/* pa_prefill with the timing events of pa_decode_timed. */
+int pa_prefill_timed(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+                     int32_t chunk_len, const uint16_t *q, uint16_t *out, float softmax_scale,
+                     int32_t num_partitions, uint32_t *flags, void *workspace,
+                     size_t workspace_bytes, pa_stream_t stream, pa_event_t const events[4]);
+
+/* Workspace bytes of pa_prefill; (size_t)-1 for invalid arguments. */
+size_t pa_prefill_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                                  int32_t num_q_heads, int32_t chunk_len, int32_t num_partitions);
+
+/* Partitions pa_prefill will use (after the automatic choice when 0). */
+int pa_prefill_num_partitions(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                              int32_t num_q_heads, int32_t chunk_len, int32_t num_partitions);
 
 /* Workspace bytes of pa_decode_multi; (size_t)-1 for invalid or unsupported
  * arguments.  The partition count is pa_decode_num_partitions' (q_len does

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror",
               "pa_decode_multi", "pa_decode_multi_workspace_bytes", "pa_decode_scored",
-              "pa_cache_compact"):
+              "pa_cache_compact", "pa_prefill", "pa_prefill_workspace_bytes"):
         assert n in names
 
 
@@ -201,6 +201,29 @@ def test_compact_rejects_bad_arguments():
     assert cp(scores=FAKE + 1) == -1
     assert cp(fl=FAKE + 2) == -1
     assert cp(cc=_cache(head_dim=80)) == -2
+
+
+def test_prefill_arguments_and_partitions():
+    L = pa.lib()
+    c = _cache()
+    s = _seq(batch=4, table_width=2048)
+    pf = lambda hq=32, cl=2048, parts=0, ws=None, ws_bytes=0: L.pa_prefill(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(s), hq, cl, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        0.088, parts, None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert pf(cl=0) == -1
+    assert pf(cl=2048 * 16 + 1) == -1                     # longer than the table holds
+    assert pf(hq=8 * 17) == -2
+    n = lambda cl, p: L.pa_prefill_num_partitions(ctypes.byref(c), ctypes.byref(s), 32, cl, p)  # noqa: E731
+    # 4 x 8 units x (4 heads x 2048 tokens / 64) column blocks = 4096 waves: no split
+    assert n(2048, 0) == 1
+    # a short chunk gives few waves (32): the prefix is split into 64 partitions
+    # of 32 pages (about 2048 waves, partitions no shorter than 32 pages)
+    assert n(16, 0) == 64
+    assert n(2048, 3) == 3
+    wsb = lambda cl, p: L.pa_prefill_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, cl, p)  # noqa: E731
+    assert wsb(2048, 1) == 0
+    assert wsb(64, 2) == 4 * 64 * 32 * 2 * 128 * 4 + 4 * 64 * 32 * 2 * 2 * 4
+    assert pf(parts=2, cl=64, ws=FAKE, ws_bytes=wsb(64, 2) - 1) == -3
 
 
 def test_append_rejects_bad_arguments():
