@@ -72,22 +72,35 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 // ----------------------------------------------------------- compaction
-// One workgroup per (unit, destination page).  Token s of destination page j
-// is kept token j*16 + s of the unit.  Invalid positions and page ids are
-// skipped here (the flags kernel reports them).
+// One wave per (unit, destination page); token s of destination page j is
+// kept token j*16 + s of the unit.  Lanes 0..15 look up their token's source
+// (old block, slot, FP8 scales) and every chunk reads it from them by lane
+// shuffle, so a wave needs no LDS and no barrier, and four independent pages
+// share each workgroup.  Work goes by 16-byte chunks of the destination
+// blocks (the layout pa.h documents), 2 * BLOCK / 1024 chunks per lane:
+//   a K chunk holds 16/E consecutive dims of one token, so it comes whole
+//   from one chunk of the token's old block;
+//   a V chunk holds, for one dim column c and 4 consecutive tokens, 4/E tiles
+//   of 4 tokens; its 4 tokens come from 4 old chunks (possibly 4 old pages),
+//   4/E elements each.
+// FP8 values are decoded under their old page's scale; the new page's K and
+// V amax are reduced over the wave, then every chunk is re-encoded.  Slots
+// past the kept count and tokens with an invalid position keep the bytes
+// they had (the flags kernel reports the invalid ones).
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   constexpr int E = FP8 ? 1 : 2;
-  constexpr int BLOCK_ELEMS = kPageSize * D;
-  constexpr int PER = kPageSize * D / 256;     // elements of one block per thread
-  __shared__ int s_src_blk[kPageSize];         // old block of each token (-1: skip)
-  __shared__ int s_src_vblk[kPageSize];
-  __shared__ int s_src_slot[kPageSize];
-  __shared__ float s_ksc[kPageSize], s_vsc[kPageSize];
-  __shared__ float s_red[2][4];
+  constexpr int CE = 16 / E;                   // elements per 16-byte chunk
+  constexpr int TPC = CE / 4;                  // V: tiles (dims) per chunk
+  constexpr int BLOCK = kPageSize * D * E;
+  constexpr int NCH = BLOCK / 16;              // chunks per block (K or V)
+  constexpr int CPL = 2 * NCH / 64;            // chunks per lane
 
-  const int unit = blockIdx.x / a.pages_per_unit;
-  const int j = blockIdx.x - unit * a.pages_per_unit;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = item / a.pages_per_unit;
+  if (unit >= a.batch * a.num_kv_heads) return;
+  const int j = item - unit * a.pages_per_unit;
   const int Hkv = a.num_kv_heads;
   const int b = unit / Hkv, h = unit - b * Hkv;
   const int row = a.head_layout ? unit : b;
@@ -103,91 +116,150 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   const size_t blk_new = a.head_layout ? (size_t)pid_new : (size_t)pid_new * Hkv + h;
   const size_t vblk_new = v_block_slot(pid_new, h, Hkv, a.num_pages, a.head_layout);
 
-  if (threadIdx.x < kPageSize) {
-    const int s = threadIdx.x;
-    int blk = -1, vblk = -1, slot = 0;
-    if (s < cnt) {
-      const int pos = a.keep[((size_t)unit * a.keep_stride) + j * kPageSize + s];
-      if (pos >= 0 && pos < L) {
-        const int pid = a.block_table[(size_t)row * a.table_width + pos / kPageSize];
-        if ((unsigned)pid < (unsigned)a.num_pages) {
-          blk = (int)(a.head_layout ? (size_t)pid : (size_t)pid * Hkv + h);
-          vblk = (int)v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout);
-          slot = pos % kPageSize;
-          if (FP8) {
-            s_ksc[s] = a.k_scale[blk];
-            s_vsc[s] = a.v_scale[blk];
-          }
-          if (a.scores != nullptr)
-            a.scores[blk_new * kPageSize + s] = a.scores[(size_t)blk * kPageSize + slot];
+  // lane s < cnt: the source of destination slot s (blk -1: nothing to write)
+  int my_blk = -1, my_vblk = 0, my_slot = 0;
+  float my_ksc = 0.f, my_vsc = 0.f;
+  if (lane < cnt) {
+    const int pos = a.keep[((size_t)unit * a.keep_stride) + j * kPageSize + lane];
+    if (pos >= 0 && pos < L) {
+      const int pid = a.block_table[(size_t)row * a.table_width + pos / kPageSize];
+      if ((unsigned)pid < (unsigned)a.num_pages) {
+        my_blk = (int)(a.head_layout ? (size_t)pid : (size_t)pid * Hkv + h);
+        my_vblk = (int)v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout);
+        my_slot = pos % kPageSize;
+        if (FP8) {
+          my_ksc = a.k_scale[my_blk];
+          my_vsc = a.v_scale[my_blk];
         }
       }
     }
-    s_src_blk[s] = blk;
-    s_src_vblk[s] = vblk;
-    s_src_slot[s] = slot;
   }
-  __syncthreads();
+  // The scores move last: a store issued before the gathers would be waited
+  // for with them.
+  auto move_scores = [&]() {
+    if (a.scores != nullptr && my_blk >= 0)
+      a.scores[blk_new * kPageSize + lane] = a.scores[(size_t)my_blk * kPageSize + my_slot];
+  };
 
-  if (!FP8) {
-    const uint16_t* ko = reinterpret_cast<const uint16_t*>(a.k_old);
-    const uint16_t* vo = reinterpret_cast<const uint16_t*>(a.v_old);
-    uint16_t* kn = reinterpret_cast<uint16_t*>(a.k_new) + blk_new * BLOCK_ELEMS;
-    uint16_t* vn = reinterpret_cast<uint16_t*>(a.v_new) + vblk_new * BLOCK_ELEMS;
-    for (int e = threadIdx.x; e < cnt * D; e += blockDim.x) {
-      const int s = e / D, d = e - s * D;
-      if (s_src_blk[s] < 0) continue;
-      const int so = s_src_slot[s];
-      kn[k_elem<D, E>(s, d)] = ko[(size_t)s_src_blk[s] * BLOCK_ELEMS + k_elem<D, E>(so, d)];
-      vn[v_elem<D, E>(s, d)] = vo[(size_t)s_src_vblk[s] * BLOCK_ELEMS + v_elem<D, E>(so, d)];
+  const u32x4* kold = reinterpret_cast<const u32x4*>(a.k_old);
+  const u32x4* vold = reinterpret_cast<const u32x4*>(a.v_old);
+  u32x4* knew = reinterpret_cast<u32x4*>(a.k_new) + blk_new * NCH;
+  u32x4* vnew = reinterpret_cast<u32x4*>(a.v_new) + vblk_new * NCH;
+
+  // Gather every chunk of this lane first (all loads in flight together).
+  // K chunk kc = (seg, t, q): token t, dims seg*4*CE + q*CE ... + CE - 1.
+  // V chunk vc = (jh, c, t4): element jl*4 + i is token 4*t4 + i, dim
+  // (jh*TPC + jl)*16 + c.
+  u32x4 raw[CPL];
+  uint32_t valid[CPL];
+  float esc[CPL][4];   // FP8: the source scale of the chunk's token(s)
+#pragma unroll
+  for (int r = 0; r < CPL; ++r) {
+    const int ch = r * 64 + lane;
+    raw[r] = u32x4{0u, 0u, 0u, 0u};
+    valid[r] = 0;
+    if (ch < NCH) {
+      const int t = (ch >> 2) & 15;
+      const int blk = __shfl(my_blk, t, 64);
+      const int so = __shfl(my_slot, t, 64);
+      esc[r][0] = esc[r][1] = esc[r][2] = esc[r][3] = __shfl(my_ksc, t, 64);
+      if (blk >= 0) {
+        raw[r] = kold[(size_t)blk * NCH + ((ch >> 6) << 6) + so * 4 + (ch & 3)];
+        valid[r] = (1u << CE) - 1u;
+      }
+    } else {
+      const int vc = ch - NCH;
+      const int t4 = vc & 3, colbase = vc >> 2;   // colbase = jh * 16 + c
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * t4 + i;
+        const int blk = __shfl(my_blk, t, 64);
+        const int vblk = __shfl(my_vblk, t, 64);
+        const int so = __shfl(my_slot, t, 64);
+        esc[r][i] = __shfl(my_vsc, t, 64);
+        if (blk < 0) continue;
+        const u32x4 sc = vold[(size_t)vblk * NCH + colbase * 4 + (so >> 2)];
+        // element jl*4 + i <- element jl*4 + (so & 3) of the source chunk
+#pragma unroll
+        for (int jl = 0; jl < TPC; ++jl) {
+          const int se = jl * 4 + (so & 3), de = jl * 4 + i;
+          uint32_t v;
+          if (E == 1) v = (sc[se >> 2] >> (8 * (se & 3))) & 0xFFu;
+          else v = (sc[se >> 1] >> (16 * (se & 1))) & 0xFFFFu;
+          if (E == 1) w[de >> 2] |= v << (8 * (de & 3));
+          else w[de >> 1] |= v << (16 * (de & 1));
+          valid[r] |= 1u << de;
+        }
+      }
+      raw[r] = u32x4{w[0], w[1], w[2], w[3]};
     }
+  }
+
+  // Merge `fresh` into destination chunk ch where `valid` says so.
+  auto put = [&](int ch, u32x4 fresh, uint32_t vmask) {
+    u32x4* dst = ch < NCH ? knew + ch : vnew + (ch - NCH);
+    constexpr uint32_t all = (1u << CE) - 1u;
+    if ((vmask & all) == all) {
+      *dst = fresh;
+      return;
+    }
+    if (vmask == 0) return;
+    u32x4 old = *dst;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      if (!((vmask >> e) & 1u)) continue;
+      const uint32_t m = E == 1 ? (0xFFu << (8 * (e & 3))) : (0xFFFFu << (16 * (e & 1)));
+      const int wi = E == 1 ? (e >> 2) : (e >> 1);
+      old[wi] = (old[wi] & ~m) | (fresh[wi] & m);
+    }
+    *dst = old;
+  };
+
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) put(r * 64 + lane, raw[r], valid[r]);
+    move_scores();
     return;
-  }
-
-  // FP8: x = fl32(dec(c) * s_old) for every kept value, then amax, s_new, codes.
-  float xk[PER], xv[PER];
-  float mk = 0.f, mv = 0.f;
+  } else {
+    // FP8: x = fl32(dec(c) * s_old); amax over the wave; re-encode under s_new.
+    float mk = 0.f, mv = 0.f;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int e = r * 256 + threadIdx.x;
-    const int s = e / D, d = e - s * D;
-    xk[r] = xv[r] = 0.f;
-    if (s < cnt && s_src_blk[s] >= 0) {
-      const int so = s_src_slot[s];
-      xk[r] = __fmul_rn(e4m3_to_f32(a.k_old[(size_t)s_src_blk[s] * BLOCK_ELEMS + k_elem<D, E>(so, d)]),
-                        s_ksc[s]);
-      xv[r] = __fmul_rn(e4m3_to_f32(a.v_old[(size_t)s_src_vblk[s] * BLOCK_ELEMS + v_elem<D, E>(so, d)]),
-                        s_vsc[s]);
-      mk = fmaxf(mk, fabsf(xk[r]));
-      mv = fmaxf(mv, fabsf(xv[r]));
-    }
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    mk = fmaxf(mk, __shfl_xor(mk, off, 64));
-    mv = fmaxf(mv, __shfl_xor(mv, off, 64));
-  }
-  if ((threadIdx.x & 63) == 0) {
-    s_red[0][threadIdx.x >> 6] = mk;
-    s_red[1][threadIdx.x >> 6] = mv;
-  }
-  __syncthreads();
-  mk = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-  mv = fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
-  const float sk = __fdiv_rn(mk, 448.0f), sv = __fdiv_rn(mv, 448.0f);
-  uint8_t* kn = a.k_new + blk_new * BLOCK_ELEMS;
-  uint8_t* vn = a.v_new + vblk_new * BLOCK_ELEMS;
+    for (int r = 0; r < CPL; ++r) {
+      const bool is_k = r * 64 + lane < NCH;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int e = r * 256 + threadIdx.x;
-    const int s = e / D, d = e - s * D;
-    if (s < cnt && s_src_blk[s] >= 0) {
-      kn[k_elem<D, E>(s, d)] = sk == 0.f ? (uint8_t)0 : (uint8_t)e4m3_rne_sat(__fdiv_rn(xk[r], sk));
-      vn[v_elem<D, E>(s, d)] = sv == 0.f ? (uint8_t)0 : (uint8_t)e4m3_rne_sat(__fdiv_rn(xv[r], sv));
+      for (int e = 0; e < 16; ++e) {
+        if (!((valid[r] >> e) & 1u)) continue;
+        const float x = __fmul_rn(e4m3_to_f32((raw[r][e >> 2] >> (8 * (e & 3))) & 0xFFu), esc[r][e & 3]);
+        if (is_k) mk = fmaxf(mk, fabsf(x));
+        else mv = fmaxf(mv, fabsf(x));
+      }
     }
-  }
-  if (threadIdx.x == 0) {
-    a.k_scale[blk_new] = sk;
-    a.v_scale[blk_new] = sv;
+    for (int off = 32; off >= 1; off >>= 1) {
+      mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+      mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+    }
+    const float sk = __fdiv_rn(mk, 448.0f), sv = __fdiv_rn(mv, 448.0f);
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) {
+      if (valid[r] == 0) continue;
+      const bool is_k = r * 64 + lane < NCH;
+      const float s_new = is_k ? sk : sv;
+      u32x4 enc = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (!((valid[r] >> e) & 1u)) continue;
+        const float x = __fmul_rn(e4m3_to_f32((raw[r][e >> 2] >> (8 * (e & 3))) & 0xFFu), esc[r][e & 3]);
+        const uint32_t code = s_new == 0.f ? 0u : e4m3_rne_sat(__fdiv_rn(x, s_new));
+        enc[e >> 2] |= code << (8 * (e & 3));
+      }
+      put(r * 64 + lane, enc, valid[r]);
+    }
+    if (lane == 0) {
+      a.k_scale[blk_new] = sk;
+      a.v_scale[blk_new] = sv;
+    }
+    move_scores();
   }
 }
 
@@ -237,7 +309,8 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)a.batch * a.num_kv_heads * a.pages_per_unit;
+  const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.pages_per_unit;
+  const unsigned grid = (items + 3) / 4;   // one wave per destination page
   if (grid > 0) {
     if (a.head_dim == 128) {
       if (a.fp8) hipLaunchKernelGGL((compact_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
