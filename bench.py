@@ -87,9 +87,12 @@ def algorithmic_bytes(w, check=True, scored=False):
     append = n_units * T * w.D * 2 * (2 + e)
     attn = kv + w.B * T * w.Hq * w.D * 2 + table + scales
     score = 8 * int(L.sum()) * hkv_u if scored else 0     # read-modify-write of one fp32 per token
-    return dict(kv=kv, decode=kv + qo + table + scales + tags + score, append=append,
-                step=kv + qo + table + scales + tags + append + score, attention_kernel=attn,
-                scores=score)
+    out = dict(kv=kv, decode=kv + qo + table + scales + tags + score, append=append,
+               step=kv + qo + table + scales + tags + append + score, attention_kernel=attn,
+               scores=score)
+    if scored:   # the score pass: K again, Q, the table, K scales, the scores read and written
+        out["score_pass"] = kv // 2 + w.B * T * w.Hq * w.D * 2 + table + scales // 2 + score
+    return out
 
 
 def compaction_bytes(w, n_keep_units):
@@ -392,6 +395,9 @@ def main():
             t_val.mean() * 1e3, t_attn.mean() * 1e3, " + score" if args.scored else "",
             t_red.mean() * 1e3, gbs, attn_gbs,
             100 * attn_gbs / HBM_PEAK_GBS))
+    if args.scored:
+        log("score pass (with the reduce): %.0f GB/s of its own bytes" % (
+            by["score_pass"] / (t_red.mean() * 1e-3) / 1e9))
 
     graph = None
     if not args.no_graph and not args.scored and args.prefill == 0:

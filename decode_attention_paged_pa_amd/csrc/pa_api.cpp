@@ -89,10 +89,9 @@ void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Partials [B][T][Hq][Pn] (D floats, then (max, sum)) when Pn > 1; for a
-// scored decode also the page scores [units][W][G][16] and the rows' final
-// (max, sum) [B][Hq][2].
+// scored decode also the rows' final (max, sum) [B][Hq][2].
 struct WorkspaceLayout {
-  size_t part_o = 0, part_ml = 0, logits = 0, row_ml = 0, total = 0;
+  size_t part_o = 0, part_ml = 0, row_ml = 0, total = 0;
 };
 
 WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
@@ -107,10 +106,6 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, i
     off += align256(rows * 2 * sizeof(float));
   }
   if (scored) {
-    const size_t units = (size_t)s->batch * c->num_kv_heads;
-    const size_t group = (size_t)hq / c->num_kv_heads;
-    w.logits = off;
-    off += align256(units * s->table_width * group * pa::kPageSize * sizeof(float));
     w.row_ml = off;
     off += align256((size_t)s->batch * hq * 2 * sizeof(float));
   }
@@ -121,6 +116,28 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, i
 size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len,
                      int parts, bool scored = false) {
   return workspace_layout(c, s, hq, q_len, parts, scored).total;
+}
+
+// Eviction score pass: K-only streaming, one wave per run of pages; runs of
+// 16 to kMassRun pages (the wave's LDS rows), enough of them for about
+// kMassTargetWaves waves.
+#ifndef PA_MASS_WAVES
+#define PA_MASS_WAVES 4096
+#endif
+constexpr int64_t kMassTargetWaves = PA_MASS_WAVES;
+
+void choose_mass_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int* chunk_pages,
+                            int* num_parts) {
+  const int W = s->table_width;
+  const int64_t units = (int64_t)s->batch * c->num_kv_heads;
+  int64_t p = (kMassTargetWaves + units - 1) / units;
+  const int64_t pmin = (W + pa::kMassRun - 1) / pa::kMassRun;
+  const int64_t pmax = (W + 15) / 16;
+  p = p > pmax ? pmax : p;
+  p = p < pmin ? pmin : p;
+  const int cp = (int)((W + p - 1) / p);
+  *chunk_pages = cp;
+  *num_parts = (W + cp - 1) / cp;
 }
 
 // Chunked prefill: a unit's G * T query columns go in blocks of 64, one wave
@@ -223,10 +240,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
     a.part_o = reinterpret_cast<float*>(ws + wl.part_o);
     a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
   }
-  if (scores) {
-    a.logits = reinterpret_cast<float*>(ws + wl.logits);
-    a.row_ml = reinterpret_cast<float*>(ws + wl.row_ml);
-  }
+  if (scores) a.row_ml = reinterpret_cast<float*>(ws + wl.row_ml);
   a.batch = seq->batch;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = cache->num_kv_heads;
@@ -251,22 +265,11 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (parts > 1) {
     if (pa::launch_reduce(a, cache->head_dim, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
-  if (scores) {
-    pa::ScoreArgs sa{};
-    sa.logits = a.logits;
-    sa.row_ml = a.row_ml;
-    sa.block_table = seq->block_table;
-    sa.lens = seq->lens;
-    sa.flags = flags;
-    sa.scores = scores;
-    sa.batch = seq->batch;
-    sa.num_kv_heads = cache->num_kv_heads;
-    sa.group = a.group;
-    sa.num_q_heads = num_q_heads;
-    sa.table_width = seq->table_width;
-    sa.num_pages = cache->num_pages;
-    sa.head_layout = head;
-    if (pa::launch_score(sa, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  if (scores) {   // second pass: K again, with the rows' final (max, sum)
+    pa::AttnArgs m = a;
+    m.scores = scores;
+    choose_mass_partitions(cache, seq, &m.chunk_pages, &m.num_parts);
+    if (pa::launch_mass(m, cache->head_dim, fp8, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   rec(3);
   return PA_OK;

@@ -148,17 +148,9 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
 // the scores of the last page or two per column.  Every K and V fragment is
 // converted once and multiplied into all NQ tiles.
 //
-// SCORE (decode only) also writes every page's log2-domain scores, and the
-// final (max, sum) of single-partition rows, for the eviction score update
-// ("Making Workers AI faster and more efficient", KV cache compression
-// section: evict the entries with the least accumulated attention).  The
-// weights themselves need the final max and sum of the whole row, known only
-// after the reduce, so the scores go out and a later kernel normalises them.
-// Measured on the 32K-token FP8 workload, that write stream (G * 64 bytes per
-// page and head, 537 MB) costs about 45% of the kernel time whatever its
-// shape: per-page stores, 8 KiB bursts gathered in LDS, non-temporal stores
-// and half the bytes all land within 10% of each other.
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SCORE = false>
+// With a.row_ml set (scored decode), single-partition rows also keep their
+// final (max, sum) there for the eviction score pass (mass_kernel below).
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
 __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
   constexpr int E = FP8 ? 1 : 2;               // bytes per cached element
   constexpr int BLOCK = kPageSize * D * E;     // bytes of one (page, head) block
@@ -414,12 +406,6 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim[nq]) ? sc[r] : -INFINITY;
       }
-      if constexpr (SCORE) {
-        // [unit][page][g][16 tokens]: the valid columns' lanes write one 16-byte chunk each
-        if (c < G)
-          *reinterpret_cast<f32x4*>(a.logits + (((size_t)unit * a.table_width + page) * G + c) * 16 +
-                                    4 * q4) = f32x4{sc[0], sc[1], sc[2], sc[3]};
-      }
       float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mloc = col_max(mloc);
       if (__builtin_amdgcn_ballot_w64(mloc > m_run[nq] + kRescaleSlack)) {
@@ -495,11 +481,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       if (cc < cend) {
         const size_t qrow = col_row(cc);
         if (Pn == 1) {
-          if constexpr (SCORE) {
-            if (q4 == 0) {
-              a.row_ml[qrow * 2 + 0] = m_run[nq];
-              a.row_ml[qrow * 2 + 1] = l_tot;
-            }
+          if (a.row_ml != nullptr && q4 == 0) {   // scored decode: the row's final (max, sum)
+            a.row_ml[qrow * 2 + 0] = m_run[nq];
+            a.row_ml[qrow * 2 + 1] = l_tot;
           }
           const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
 #pragma unroll
@@ -672,7 +656,7 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SCORE = false>
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   const int ppw = NQ == 1 ? a.parts_per_wave : 1;
   const unsigned groups = (unsigned)(a.num_parts + ppw - 1) / ppw;
@@ -684,7 +668,7 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.col_blocks * groups;
     grid = (items + kWaves - 1) / kWaves;
   }
-  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL, SCORE>), dim3(grid),
+  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL>), dim3(grid),
                      dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
@@ -693,12 +677,225 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
 // rounded up to 1, 2 or 4.
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_attention_q(const AttnArgs& a, hipStream_t s) {
-  if (a.logits) return launch_attention_t<D, FP8, HEAD, 1, false, true>(a, s);  // decode only
   if (a.q_len == 1) return launch_attention_t<D, FP8, HEAD, 1, false>(a, s);
   const int cols = a.group * a.q_len;
   if (cols <= 16) return launch_attention_t<D, FP8, HEAD, 1, true>(a, s);
   if (cols <= 32) return launch_attention_t<D, FP8, HEAD, 2, true>(a, s);
   return launch_attention_t<D, FP8, HEAD, 4, true>(a, s);
+}
+
+// ------------------------------------------------------ eviction scores
+// Second pass of a scored decode step, for the eviction policy of "Making
+// Workers AI faster and more efficient" (KV cache compression section: the
+// entries that have drawn the least attention go first).  The weight of token
+// j in row (b, query head) is exp2(s_j - M) / L, with (M, L) the row's final
+// log2-domain max and sum: they exist only once the decode and its reduce have
+// finished.  This kernel reads the K pages again, recomputes the scores with
+// the attention kernel's operands and MFMA sequence (so s is bitwise the same),
+// and adds each token's weights, summed over the G query heads of its KV head,
+// to the paged score array.  Rereading K (half the decode's bytes) costs less
+// than writing every score out of the decode and reading it back: G * 64 bytes
+// per page and head each way, a write stream that measured about 45% of the
+// decode kernel's time when it ran inside it.
+//
+// One wave per (unit, run of chunk_pages <= 128 pages), heads fastest, so a
+// workgroup's four waves read neighbouring head blocks of the same pages.
+// Lane (c, q4) owns query head c and tokens 4*q4 .. 4*q4+3 of each page; the
+// sum over heads is a butterfly across the 16 lanes of a DPP row (fixed
+// order: deterministic).  The page's 16 sums go to the wave's own LDS rows,
+// and the scores are read, added to and written once, after the run's last
+// page.  A score access inside the page loop stalls the K stream: vector
+// loads and stores share one in-order completion counter, so the next K wait
+// also waits for it (measured on the 32K-token FP8 workload: reads or writes
+// of the scores every 64 pages each cost about a quarter of the kernel time).
+#ifndef PA_MASS_PIPE
+#define PA_MASS_PIPE 2         // pages held in registers per wave
+#endif
+#ifndef PA_MASS_THROTTLE
+#define PA_MASS_THROTTLE 1     // wait for a page's loads before requesting the next
+#endif
+static_assert(PA_MASS_PIPE >= 2 && PA_MASS_PIPE <= 6, "pipeline depth");
+
+// Sum over the 16 lanes of each DPP row; every lane gets the (same) total.
+__device__ inline float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+
+template <int D, bool FP8, bool HEAD>
+__global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
+  constexpr int E = FP8 ? 1 : 2;
+  constexpr int BLOCK = kPageSize * D * E;
+  constexpr int NSEG = BLOCK / 1024;
+  constexpr int NSTEP = D / 32;
+  constexpr int PIPE = PA_MASS_PIPE;
+  const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * kWaves + wave;
+  if (item >= a.batch * Hkv * a.num_parts) return;
+  const int h = item % Hkv;
+  const int rest = item / Hkv;
+  const int b = rest % a.batch;
+  const int part = rest / a.batch;
+  if (a.flags != nullptr && a.flags[b] != 0u) return;   // aborted request: no update
+  const int unit = b * Hkv + h;
+  const int row = HEAD ? unit : b;
+  const int cap = a.table_width * kPageSize;
+  int L = a.lens[row];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int npages = (L + kPageSize - 1) / kPageSize;
+  const int p0 = part * a.chunk_pages;
+  const int p1 = min(p0 + a.chunk_pages, npages);
+  if (p0 >= p1) return;
+  const int n = min(p1 - p0, kMassRun);   // the host's runs are never longer
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, q4 = lane >> 4;
+  const bool col = c < G;
+  const size_t qrow = (size_t)b * Hq + h * G + (col ? c : 0);
+
+  // Q^T operand and the lane's row (max, 1/sum), as in the attention kernel
+  bf16x8 qop[NSTEP];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    const int d0 = FP8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4;
+    u32x4 v = *reinterpret_cast<const u32x4*>(a.q + qrow * D + d0);
+    if (!col) v = u32x4{0u, 0u, 0u, 0u};
+    qop[s] = __builtin_bit_cast(bf16x8, v);
+  }
+  const float M = a.row_ml[qrow * 2 + 0];
+  const float inv = 1.f / a.row_ml[qrow * 2 + 1];
+
+  const int32_t* bt = a.block_table + (size_t)row * a.table_width + p0;
+  const size_t page_stride = HEAD ? (size_t)BLOCK : (size_t)Hkv * BLOCK;
+  const uint8_t* kpool = a.k_pages + (HEAD ? 0 : (size_t)h * BLOCK);
+  const float* kscale = FP8 ? a.k_scale + (HEAD ? 0 : h) : nullptr;
+  const int scale_stride = HEAD ? 1 : Hkv;
+  const int lane_off = (c * 4 + q4) * 16;
+
+  // The run's page ids (and FP8 scales), one lane per page, loaded and waited
+  // for before the page loop (see the attention kernel).
+  constexpr int kIdRegs = kMassRun / 64;
+  int ids[kIdRegs];
+  float sks[FP8 ? kIdRegs : 1];
+#pragma unroll
+  for (int j = 0; j < kIdRegs; ++j) {
+    const int k = 64 * j + lane;
+    ids[j] = k < n ? bt[k] : 0;
+  }
+  int last = __builtin_amdgcn_readfirstlane(ids[kIdRegs - 1]);
+  asm volatile("" : : "s"(last));
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < kIdRegs; ++j) {
+      const int pid = (unsigned)ids[j] < (unsigned)a.num_pages ? ids[j] : 0;
+      sks[j] = kscale[(size_t)pid * scale_stride];
+    }
+  }
+  static_assert(kIdRegs == 2, "one register per 64 pages");
+  auto lane_reg = [&](const auto (&v)[kIdRegs], int r) { return r < 64 ? v[0] : v[1]; };
+
+  u32x4 kr[PIPE][NSEG];
+  float ks[PIPE];
+  auto load = [&](int slot, int r) {   // r: page within the run, uniform
+    const int raw = __builtin_amdgcn_readlane(lane_reg(ids, r), r & 63);
+    const int pid = (unsigned)raw < (unsigned)a.num_pages ? raw : 0;
+    const uint8_t* kp = kpool + (size_t)pid * page_stride;
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) kr[slot][i] = load16(kp + lane_off + i * 1024);
+    if constexpr (FP8)
+      ks[slot] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_reg(sks, r)), r & 63));
+  };
+
+  // The run's score sums: row k holds page k's 16 tokens.
+  __shared__ f32x4 s_mass[kWaves][kMassRun][4];
+  f32x4 (*mass)[4] = s_mass[wave];
+
+  auto compute = [&](int slot, int k) {
+    const int page = p0 + k;
+    float kfac = a.score_scale_log2;
+    if (FP8) kfac *= ks[slot];
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      if (FP8) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x2 lo = fp8x4_to_bf16x4(kr[slot][i][2 * hh]);
+          u32x2 hi = fp8x4_to_bf16x4(kr[slot][i][2 * hh + 1]);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qop[2 * i + hh], acc, 0, 0, 0);
+        }
+      } else {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, kr[slot][i]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qop[i], acc, 0, 0, 0);
+      }
+    }
+    const int tok0 = page * kPageSize + q4 * 4;
+    f32x4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sc = acc[r] * kfac;
+      w[r] = (col && tok0 + r < L) ? __builtin_amdgcn_exp2f(sc - M) * inv : 0.f;
+      w[r] = row16_sum(w[r]);
+    }
+    if (c == 0) mass[k][q4] = w;
+  };
+
+  // Register ring of PIPE pages with the attention kernel's throttle (one
+  // page in flight besides the one being consumed: measured best here too).
+#pragma unroll
+  for (int u = 0; u < PIPE - 1; ++u) load(u, min(u, n - 1));
+  for (int r0 = 0; r0 < n; r0 += PIPE) {
+#pragma unroll
+    for (int u = 0; u < PIPE; ++u) {
+      const int r = r0 + u;
+      if constexpr (PA_MASS_THROTTLE) __builtin_amdgcn_s_waitcnt(0x0F70);   // s_waitcnt vmcnt(0)
+      load((u + PIPE - 1) % PIPE, min(r + PIPE - 1, n - 1));
+      if (r < n) compute(u, r);
+    }
+  }
+
+  // The run's scores, 16 pages per instruction: lane (page k = 16 * it +
+  // lane / 4, quarter e = lane % 4) reads, adds and writes tokens 4e .. 4e+3
+  // of page k, so each page's 64 bytes come from four neighbouring lanes.
+  // Ids out of range (tag check off) have no page to credit; slots past L
+  // keep their bits.
+  constexpr int kIt = kMassRun / 16;
+  const int e = lane & 3;
+  f32x4 v[kIt];
+  float* dst[kIt];
+  int valid[kIt];   // tokens of the lane's page below L; <= 0: nothing to do
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int k = 16 * it + (lane >> 2);
+    const int id = __shfl(ids[it >> 2], k & 63);
+    const bool live = k < n && (unsigned)id < (unsigned)a.num_pages;
+    valid[it] = live ? L - (p0 + k) * kPageSize : 0;
+    const size_t slot0 = HEAD ? (size_t)(live ? id : 0) * kPageSize
+                              : ((size_t)(live ? id : 0) * Hkv + h) * kPageSize;
+    dst[it] = a.scores + slot0 + 4 * e;
+    v[it] = live ? *reinterpret_cast<const f32x4*>(dst[it]) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (valid[it] <= 0) continue;
+    const f32x4 add = mass[16 * it + (lane >> 2)][e];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (4 * e + t < valid[it]) v[it][t] += add[t];
+    *reinterpret_cast<f32x4*>(dst[it]) = v[it];   // each (page, head, slot) belongs to one unit
+  }
+}
+
+template <int D, bool FP8, bool HEAD>
+hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
+  const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.num_parts;
+  hipLaunchKernelGGL((mass_kernel<D, FP8, HEAD>), dim3((items + kWaves - 1) / kWaves),
+                     dim3(64 * kWaves), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -732,6 +929,15 @@ hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipS
     else hipLaunchKernelGGL((reduce_kernel<64, false>), dim3(grid), dim3(64), 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_mass(const AttnArgs& a, int head_dim, bool fp8, bool head_layout, hipStream_t s) {
+  if (head_dim == 128) {
+    if (fp8) return head_layout ? launch_mass_t<128, true, true>(a, s) : launch_mass_t<128, true, false>(a, s);
+    return head_layout ? launch_mass_t<128, false, true>(a, s) : launch_mass_t<128, false, false>(a, s);
+  }
+  if (fp8) return head_layout ? launch_mass_t<64, true, true>(a, s) : launch_mass_t<64, true, false>(a, s);
+  return head_layout ? launch_mass_t<64, false, true>(a, s) : launch_mass_t<64, false, false>(a, s);
 }
 
 }  // namespace pa

@@ -2,10 +2,10 @@
 // "KV cache compression goes open source"): the cache drops the KV entries
 // that past attention used least, like a least-frequently-used policy, and
 // the per-head block table lets each head keep a different number of tokens.
+// The scores themselves (fp32, stored like the pages, [P][heads][S], so a
+// token's score moves with its page) are updated by the decode's second pass
+// (mass_kernel, with the decode kernels).
 //
-//   score_kernel    adds a decode step's attention mass per cached token to
-//                   fp32 scores stored like the pages ([P][heads][S]), so a
-//                   token's score moves with its page;
 //   compact_kernel  rewrites the tokens each unit keeps, in order, into the
 //                   pages of a new table (FP8: decoded under the old page
 //                   scale, re-quantised under the new page's own scale);
@@ -19,57 +19,6 @@ namespace pa {
 namespace {
 
 #pragma clang fp contract(off)
-
-// --------------------------------------------------------------- scores
-// Workgroup (unit, group of 16 pages).  The mass of a token is
-// sum_g exp2(s_g - M_g) / L_g over the G query heads of the unit, with
-// (M_g, L_g) the row's final log2-domain max and sum, and s_g the score the
-// attention kernel wrote for that token.  The 16 pages' scores are one
-// contiguous run of 16 * G * 16 floats: they are read in 16-byte chunks by
-// consecutive threads, turned into weights in LDS, then summed over g in a
-// fixed order (deterministic) by one thread per token.
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  __shared__ float s_m[kMaxGroup], s_inv[kMaxGroup];
-  __shared__ f32x4 s_w[16 * kMaxGroup * 4];
-  const int unit = blockIdx.x;
-  const int Hkv = a.num_kv_heads, G = a.group;
-  const int b = unit / Hkv, h = unit - b * Hkv;
-  const int row = a.head_layout ? unit : b;
-  if (a.flags != nullptr && a.flags[b] != 0u) return;   // aborted request: no update
-  const int cap = a.table_width * kPageSize;
-  int L = a.lens[row];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int npages = (L + kPageSize - 1) / kPageSize;
-  const int i0 = blockIdx.y * 16;                        // first page of this workgroup
-  if (i0 >= npages) return;
-  const int np = min(16, npages - i0);
-  if (threadIdx.x < G) {
-    const size_t qrow = (size_t)b * a.num_q_heads + h * G + threadIdx.x;
-    s_m[threadIdx.x] = a.row_ml[qrow * 2 + 0];
-    s_inv[threadIdx.x] = 1.f / a.row_ml[qrow * 2 + 1];
-  }
-  __syncthreads();
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.logits + ((size_t)unit * a.table_width + i0) * G * 16);
-  for (int i = threadIdx.x; i < np * G * 4; i += blockDim.x) {
-    const int g = (i >> 2) % G;
-    const f32x4 v = src[i];
-    f32x4 wt;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wt[r] = __builtin_amdgcn_exp2f(v[r] - s_m[g]) * s_inv[g];
-    s_w[i] = wt;
-  }
-  __syncthreads();
-  const int pl = threadIdx.x >> 4, slot = threadIdx.x & 15;
-  const int t = (i0 + pl) * kPageSize + slot;
-  if (pl >= np || t >= L) return;
-  const int pid = a.block_table[(size_t)row * a.table_width + i0 + pl];
-  if ((unsigned)pid >= (unsigned)a.num_pages) return;   // no page to credit (unchecked ids)
-  const float* w = reinterpret_cast<const float*>(s_w) + pl * G * 16 + slot;
-  float mass = 0.f;
-  for (int g = 0; g < G; ++g) mass += w[g * 16];
-  float* sc = a.scores + ((a.head_layout ? (size_t)pid : (size_t)pid * Hkv + h) * kPageSize + slot);
-  *sc = *sc + mass;   // each (page, head, slot) belongs to exactly one unit
-}
 
 // ----------------------------------------------------------- compaction
 // One wave per (unit, destination page); token s of destination page j is
@@ -301,12 +250,6 @@ __global__ __launch_bounds__(256) void compact_flags_kernel(CompactArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.batch * a.num_kv_heads, (unsigned)(a.table_width + 15) / 16);
-  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.pages_per_unit;

@@ -11,6 +11,7 @@ constexpr int kWaves = 4;          // waves (independent work items) per attenti
 constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
 constexpr int kMaxQLen = 8;        // query tokens per sequence in one multi-query call
 constexpr int kMaxCols = 64;       // query columns (heads x tokens) per unit: 4 MFMA tiles
+constexpr int kMassRun = 128;      // pages per wave of the eviction score pass (LDS rows)
 
 // Arguments of the attention (partial) kernel.
 struct AttnArgs {
@@ -28,8 +29,8 @@ struct AttnArgs {
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int q_len;                 // query tokens per sequence (1: decode; > 1: causal drafts)
   int col_blocks;            // blocks of 64 query columns per unit (prefill chunks); else 1
-  float* logits;             // scored decode: [units][W][G][16] log2-domain scores, else nullptr
   float* row_ml;             // scored decode: [B][Hq][2] final max (log2) and sum per row
+  float* scores;             // eviction score pass: [P][Hkv (SEQ) or 1 (HEAD)][S] page scores
   int chunk_pages, num_parts;
   int parts_per_wave;        // consecutive partitions of one unit a wave streams through
   int xcd_order;             // workgroup order that keeps a page's heads on one XCD
@@ -60,19 +61,6 @@ struct AppendArgs {
   int batch, num_kv_heads, head_dim, table_width, num_pages, n_max;
   int pages_per_unit;         // ceil(n_max / S) + 1: grid slots per unit
   bool head_layout, fp8;
-};
-
-// Eviction score update: adds each token's attention mass (softmax weights
-// summed over the G query heads of its KV head) to the paged score array.
-struct ScoreArgs {
-  const float* logits;       // as AttnArgs::logits
-  const float* row_ml;       // as AttnArgs::row_ml
-  const int32_t* block_table;
-  const int32_t* lens;
-  const uint32_t* flags;     // nullptr: nothing flagged
-  float* scores;             // [P][Hkv (SEQ) or 1 (HEAD)][S]
-  int batch, num_kv_heads, group, num_q_heads, table_width, num_pages;
-  bool head_layout;
 };
 
 // Compaction after eviction: the kept tokens of each unit, in list order, are
@@ -118,7 +106,7 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head
                             hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_mass(const AttnArgs& a, int head_dim, bool fp8, bool head_layout, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 }  // namespace pa

@@ -298,12 +298,14 @@ size_t pa_decode_multi_workspace_bytes(const pa_cache_desc *cache, const pa_seq_
  *           in place (the caller zeroes a page's scores when it reallocates
  *           it).  Flagged sequences, slots past lens[u] and pages outside the
  *           pool (unchecked ids) are not touched.
- * The weights are those of the full softmax over the unit's tokens, computed
- * from the same fp32 scores the attention used, normalised with the row's
- * final max and sum after the partition merge.
+ * The weights are those of the full softmax over the unit's tokens: after
+ * the decode, a second pass reads the K pages again, recomputes the same fp32
+ * scores the attention used (bitwise) and normalises them with the row's
+ * final max and sum.  The sum over the query heads runs in a fixed order, so
+ * repeated calls give the same bits.  num_partitions splits the decode
+ * pass; the score pass splits the pages its own way.
  * Workspace: pa_decode_scored_workspace_bytes(...) bytes, never 0 (the
- * scores of every page are staged there: B * Hkv * table_width * (Hq/Hkv) *
- * 64 bytes, plus the partials of pa_decode and B * Hq * 8 bytes).
+ * partials of pa_decode plus the rows' final max and sum, B * Hq * 8 bytes).
  * Data races: two concurrent calls on the same scores array race.
  */
 int pa_decode_scored(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,

@@ -175,8 +175,8 @@ def test_decode_scored_arguments_and_workspace():
     assert sc(scores=0) == -1
     assert sc(scores=FAKE + 2) == -1
     need1 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 1)
-    # page scores [B*Hkv][W][G][16] fp32 + rows' (max, sum) [B][Hq][2]; no partials at Pn = 1
-    assert need1 == 4 * 8 * 64 * 4 * 16 * 4 + 4 * 32 * 2 * 4
+    # the rows' final (max, sum) [B][Hq][2] fp32; no partials at Pn = 1
+    assert need1 == 4 * 32 * 2 * 4
     need4 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
     assert need4 == need1 + L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
     assert sc(ws=None) == -3                                  # always needs a workspace

@@ -2,7 +2,7 @@
 
 Scored decode: outputs bit-identical to pa_decode at the same partition
 count; every score slot a unit reads grows by the oracle's attention mass
-(relative error <= 1e-4: the logits, the exp2 and the row sums are fp32,
+(relative error <= 1e-4: the scores, the exp2 and the row sums are fp32,
 each ~1e-6 relative, and the mass of a token is a sum of G such products);
 every other slot (flagged sequences, past L, unread pages) is unchanged
 bit for bit.  Compaction: pool bytes, FP8 scales and moved scores bit-exact
@@ -104,12 +104,12 @@ def test_scored_two_steps_accumulate_and_flagged_untouched():
 
 def test_scored_fp8():
     w = make_workload(3, batch=4, lens=[5, 700, 2049, 5000], stale_frac=0.0)
-    scored_case(w, seqs=range(4), partitions=(0, 4))
+    scored_case(w, seqs=range(4), partitions=(0, 1, 4))   # 1: a 313-page run, two id segments
 
 
 def test_scored_headwise():
     lens = np.array([[33, 1, 512, 16, 17, 100, 5, 64], [2048, 8, 4096, 4097, 15, 16, 31, 1000]])
-    scored_case(make_workload(4, lens=lens), seqs=range(2), partitions=(0, 16, 64))
+    scored_case(make_workload(4, lens=lens), seqs=range(2), partitions=(0, 1, 16, 64))
 
 
 def test_scored_workload5_full_size_sampled():
