@@ -469,11 +469,12 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "%s: B=%d, Hq=%d, Hkv=%d, D=%d, page 16, L=%s, %s KV, %s layout, "
-                        "split-K %d, tag check %s%s" % (
+                        "split-K %s, tag check %s%s" % (
                             w.name, w.B, w.Hq, w.Hkv, w.D,
                             "32768" if args.config == 5 else "drawn",
                             "FP8 e4m3" if w.kv_dtype == "fp8" else "BF16", w.layout.upper(),
-                            n_parts, "on" if check else "off",
+                            n_parts if n_parts > 0 else "balanced on the device",
+                            "on" if check else "off",
                             ("" if T == 1 else ", %d draft tokens per sequence (causal)" % T)
                             + (", eviction scores updated" if args.scored else "")),
             "q_len": T,

@@ -88,18 +88,75 @@ void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Partials [B][T][Hq][Pn] (D floats, then (max, sum)) when Pn > 1; for a
-// scored decode also the rows' final (max, sum) [B][Hq][2].
+// How a call splits each unit's pages.  Fixed: chunk_pages per partition,
+// parts partitions (an explicit count, prefill, and tables of at most
+// kPlanMinChunk pages).  Planned (automatic decode): plan_kernel picks the
+// chunk on the device from the real lengths, for about kTargetWaves waves of
+// equal work; a plan holds at most max_pairs (group, partition) pairs.
+#ifndef PA_PLAN_WAVES
+#define PA_PLAN_WAVES 2048
+#endif
+#ifndef PA_PLAN_MIN_CHUNK
+#define PA_PLAN_MIN_CHUNK 32
+#endif
+constexpr int64_t kPlanWaves = PA_PLAN_WAVES;      // waves of equal work the plan aims for
+constexpr int kPlanMinChunk = PA_PLAN_MIN_CHUNK;   // pages; below this a wave's fixed costs weigh
+
+struct Split {
+  bool planned = false;
+  int chunk_pages = 1, parts = 1, ppw = 1;
+  int groups = 0, hpg = 1, max_pairs = 0;   // planned only
+};
+
+Split decode_split(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req) {
+  Split sp;
+  if (req == 0 && s->table_width > kPlanMinChunk) {
+    const bool head = c->layout == PA_LAYOUT_HEAD;
+    sp.planned = true;
+    sp.hpg = head ? 1 : c->num_kv_heads;
+    sp.groups = head ? s->batch * c->num_kv_heads : s->batch;
+    // pairs <= pages / chunk + groups, and chunk >= pages * hpg / kPlanWaves
+    sp.max_pairs = (int)((kPlanWaves + sp.hpg - 1) / sp.hpg) + sp.groups;
+    return sp;
+  }
+  choose_partitions(c, s, req, &sp.chunk_pages, &sp.parts, &sp.ppw);
+  return sp;
+}
+
+void choose_prefill_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
+                               int32_t q_len, int32_t req, int* chunk_pages, int* num_parts);
+
+Split prefill_split(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len,
+                    int32_t req) {
+  Split sp;
+  choose_prefill_partitions(c, s, hq, q_len, req, &sp.chunk_pages, &sp.parts);
+  return sp;
+}
+
+// Partials: fixed partitions [B][T][Hq][Pn] (D floats, then (max, sum)) when
+// Pn > 1; planned, [pair][head in group][T * G columns] plus the plan
+// (int32: chunk, pair count, groups + 1 first pairs, the group of each pair).
+// A scored decode also keeps the rows' final (max, sum) [B][Hq][2].
 struct WorkspaceLayout {
-  size_t part_o = 0, part_ml = 0, row_ml = 0, total = 0;
+  size_t part_o = 0, part_ml = 0, plan = 0, plan_group = 0, row_ml = 0, total = 0;
 };
 
 WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
-                                 int32_t q_len, int parts, bool scored) {
+                                 int32_t q_len, const Split& sp, bool scored) {
   WorkspaceLayout w;
   size_t off = 0;
-  if (parts > 1) {
-    const size_t rows = (size_t)s->batch * q_len * hq * parts;
+  if (sp.planned) {
+    const size_t slots = (size_t)sp.max_pairs * sp.hpg * (hq / c->num_kv_heads) * q_len;
+    w.part_o = off;
+    off += align256(slots * c->head_dim * sizeof(float));
+    w.part_ml = off;
+    off += align256(slots * 2 * sizeof(float));
+    w.plan = off;
+    off += align256(((size_t)sp.groups + 3) * sizeof(int32_t));
+    w.plan_group = off;
+    off += align256((size_t)sp.max_pairs * sizeof(int32_t));
+  } else if (sp.parts > 1) {
+    const size_t rows = (size_t)s->batch * q_len * hq * sp.parts;
     w.part_o = off;
     off += align256(rows * c->head_dim * sizeof(float));
     w.part_ml = off;
@@ -114,8 +171,8 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, i
 }
 
 size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int32_t q_len,
-                     int parts, bool scored = false) {
-  return workspace_layout(c, s, hq, q_len, parts, scored).total;
+                     const Split& sp, bool scored = false) {
+  return workspace_layout(c, s, hq, q_len, sp, scored).total;
 }
 
 // Eviction score pass: K-only streaming, one wave per run of pages; runs of
@@ -192,12 +249,10 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (seq->expected_tags && (!flags || !cache->page_tags)) return PA_ERR_INVALID_ARG;
   if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
   if (scores && (q_len != 1 || !aligned(scores, 4))) return PA_ERR_INVALID_ARG;
-  int chunk_pages, parts, ppw = 1;
-  if (prefill) choose_prefill_partitions(cache, seq, num_q_heads, q_len, num_partitions,
-                                         &chunk_pages, &parts);
-  else choose_partitions(cache, seq, num_partitions, &chunk_pages, &parts, &ppw);
+  const Split sp = prefill ? prefill_split(cache, seq, num_q_heads, q_len, num_partitions)
+                           : decode_split(cache, seq, num_partitions);
   const WorkspaceLayout wl =
-      workspace_layout(cache, seq, num_q_heads, q_len, parts, scores != nullptr);
+      workspace_layout(cache, seq, num_q_heads, q_len, sp, scores != nullptr);
   const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
@@ -209,8 +264,8 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   };
 
   rec(0);
+  pa::ValidateArgs v{};
   if (flags) {
-    pa::ValidateArgs v{};
     v.block_table = seq->block_table;
     v.lens = seq->lens;
     v.expected_tags = seq->expected_tags;
@@ -221,8 +276,22 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
     v.table_width = seq->table_width;
     v.num_pages = cache->num_pages;
     v.head_layout = head;
-    if (pa::launch_validate(v, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
+  char* ws = static_cast<char*>(workspace);
+  pa::PlanArgs pl{};
+  if (sp.planned) {
+    pl.lens = seq->lens;
+    pl.plan = reinterpret_cast<int32_t*>(ws + wl.plan);
+    pl.plan_group = reinterpret_cast<int32_t*>(ws + wl.plan_group);
+    pl.num_groups = sp.groups;
+    pl.heads_per_group = sp.hpg;
+    pl.table_width = seq->table_width;
+    pl.max_pairs = sp.max_pairs;
+    pl.target_waves = (int)kPlanWaves;
+    pl.min_chunk = kPlanMinChunk;
+  }
+  if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, stream) != hipSuccess)
+    return PA_ERR_LAUNCH;
   rec(1);
 
   pa::AttnArgs a{};
@@ -235,10 +304,14 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.flags = flags;
   a.q = q;
   a.out = out;
-  char* ws = static_cast<char*>(workspace);
-  if (parts > 1) {
+  if (sp.planned || sp.parts > 1) {
     a.part_o = reinterpret_cast<float*>(ws + wl.part_o);
     a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
+  }
+  if (sp.planned) {
+    a.plan = reinterpret_cast<const int32_t*>(ws + wl.plan);
+    a.plan_group = reinterpret_cast<const int32_t*>(ws + wl.plan_group);
+    a.max_pairs = sp.max_pairs;
   }
   if (scores) a.row_ml = reinterpret_cast<float*>(ws + wl.row_ml);
   a.batch = seq->batch;
@@ -249,12 +322,14 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.col_blocks = prefill ? prefill_col_blocks(cache, num_q_heads, q_len) : 1;
   a.table_width = seq->table_width;
   a.num_pages = cache->num_pages;
-  a.chunk_pages = chunk_pages;
-  a.num_parts = parts;
-  a.parts_per_wave = ppw;
+  a.chunk_pages = sp.chunk_pages;
+  a.num_parts = sp.parts;
+  a.parts_per_wave = sp.ppw;
   // XCD-aware workgroup order needs whole groups of 4 heads; the SEQ layout
-  // gains most from it (the heads of a page share its blocks and scales).
-  a.xcd_order = (cache->num_kv_heads % pa::kWaves == 0 && a.col_blocks == 1) ? 1 : 0;
+  // gains most from it (the heads of a page share its blocks and scales).  A
+  // planned HEAD split has one head per pair and keeps the plain order.
+  a.xcd_order = (cache->num_kv_heads % pa::kWaves == 0 && a.col_blocks == 1 &&
+                 !(sp.planned && head)) ? 1 : 0;
 #ifdef PA_NO_XCD_ORDER
   a.xcd_order = 0;
 #endif
@@ -262,12 +337,14 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (pa::launch_attention(a, cache->head_dim, fp8, head, stream) != hipSuccess)
     return PA_ERR_LAUNCH;
   rec(2);
-  if (parts > 1) {
+  if (sp.planned || sp.parts > 1) {
     if (pa::launch_reduce(a, cache->head_dim, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (scores) {   // second pass: K again, with the rows' final (max, sum)
     pa::AttnArgs m = a;
     m.scores = scores;
+    m.plan = nullptr;
+    m.plan_group = nullptr;
     choose_mass_partitions(cache, seq, &m.chunk_pages, &m.num_parts);
     if (pa::launch_mass(m, cache->head_dim, fp8, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
@@ -330,9 +407,7 @@ PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, const pa_seq
   if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
       check_heads(cache, num_q_heads) != PA_OK || num_partitions < 0)
     return (size_t)-1;
-  int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
-  return workspace_for(cache, seq, num_q_heads, 1, parts);
+  return workspace_for(cache, seq, num_q_heads, 1, decode_split(cache, seq, num_partitions));
 }
 
 PA_API size_t pa_decode_multi_workspace_bytes(const pa_cache_desc* cache, const pa_seq_desc* seq,
@@ -341,9 +416,7 @@ PA_API size_t pa_decode_multi_workspace_bytes(const pa_cache_desc* cache, const 
   if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
       check_heads(cache, num_q_heads, q_len) != PA_OK || num_partitions < 0)
     return (size_t)-1;
-  int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
-  return workspace_for(cache, seq, num_q_heads, q_len, parts);
+  return workspace_for(cache, seq, num_q_heads, q_len, decode_split(cache, seq, num_partitions));
 }
 
 PA_API int pa_decode_num_partitions(const pa_cache_desc* cache, const pa_seq_desc* seq,
@@ -353,9 +426,8 @@ PA_API int pa_decode_num_partitions(const pa_cache_desc* cache, const pa_seq_des
   if ((rc = check_seq(seq)) != PA_OK) return rc;
   if ((rc = check_heads(cache, num_q_heads)) != PA_OK) return rc;
   if (num_partitions < 0) return PA_ERR_INVALID_ARG;
-  int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
-  return parts;
+  const Split sp = decode_split(cache, seq, num_partitions);
+  return sp.planned ? 0 : sp.parts;
 }
 
 PA_API int pa_decode(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
@@ -380,9 +452,7 @@ PA_API size_t pa_decode_scored_workspace_bytes(const pa_cache_desc* cache, const
   if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
       check_heads(cache, num_q_heads) != PA_OK || num_partitions < 0)
     return (size_t)-1;
-  int cp, parts;
-  choose_partitions(cache, seq, num_partitions, &cp, &parts, nullptr);
-  return workspace_for(cache, seq, num_q_heads, 1, parts, true);
+  return workspace_for(cache, seq, num_q_heads, 1, decode_split(cache, seq, num_partitions), true);
 }
 
 PA_API int pa_decode_scored(const pa_cache_desc* cache, const pa_seq_desc* seq,
@@ -453,9 +523,8 @@ PA_API size_t pa_prefill_workspace_bytes(const pa_cache_desc* cache, const pa_se
   if (check_cache(cache) != PA_OK || check_seq(seq) != PA_OK ||
       check_prefill(cache, seq, num_q_heads, chunk_len) != PA_OK || num_partitions < 0)
     return (size_t)-1;
-  int cp, parts;
-  choose_prefill_partitions(cache, seq, num_q_heads, chunk_len, num_partitions, &cp, &parts);
-  return workspace_for(cache, seq, num_q_heads, chunk_len, parts);
+  return workspace_for(cache, seq, num_q_heads, chunk_len,
+                       prefill_split(cache, seq, num_q_heads, chunk_len, num_partitions));
 }
 
 PA_API int pa_prefill_num_partitions(const pa_cache_desc* cache, const pa_seq_desc* seq,

@@ -88,49 +88,198 @@ __device__ inline u32x4 load16(const uint8_t* p) {
 // One workgroup per sequence; integrity check of the pages it will read
 // ("Cloudflare quantizes Kimi and GLM caches for 41% faster inference",
 // integrity-check paragraph: a separate batch validation before decode reads).
-__global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
+// The table entries of all the sequence's units (HEAD: one per KV head) form
+// one flat index space, 8 entries per thread per pass with every load of a
+// pass issued before any is used: two dependent round trips per 8192 entries,
+// whatever the number of units.
+constexpr int kValUnits = 64;   // units whose entry offsets are held at a time
+
+__device__ void validate_block(const ValidateArgs& a, int b) {
   __shared__ uint32_t s_bits;
-  const int b = blockIdx.x;
-  if (threadIdx.x == 0) s_bits = 0;
-  __syncthreads();
+  __shared__ int s_off[kValUnits + 1];
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bits = 0;
   uint32_t bits = 0;
   const int cap = a.table_width * kPageSize;
   const int n_units = a.head_layout ? a.num_kv_heads : 1;
-  for (int u = 0; u < n_units; ++u) {
-    const int row = a.head_layout ? b * a.num_kv_heads + u : b;
-    int L = a.lens[row];
-    if (L > cap || L < 0) bits |= 4u;
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int n = (L + kPageSize - 1) / kPageSize;
-    const int32_t* bt = a.block_table + (size_t)row * a.table_width;
-    const uint32_t* ex = a.expected_tags ? a.expected_tags + (size_t)row * a.table_width : nullptr;
-    // 8 entries per thread per pass, all loads of a pass issued before any
-    // is used: two dependent round trips per pass instead of two per entry.
+  for (int u0 = 0; u0 < n_units; u0 += kValUnits) {
+    const int nu = min(kValUnits, n_units - u0);
+    if (tid < nu) {
+      const int row = a.head_layout ? b * a.num_kv_heads + u0 + tid : b;
+      int L = a.lens[row];
+      if (L > cap || L < 0) bits |= 4u;
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      s_off[tid + 1] = (L + kPageSize - 1) / kPageSize;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      s_off[0] = 0;
+      for (int i = 1; i <= nu; ++i) s_off[i] += s_off[i - 1];
+    }
+    __syncthreads();
+    const int total = s_off[nu];
     constexpr int kPer = 8;
-    for (int base = 0; base < n; base += kPer * blockDim.x) {
+    for (int base = 0; base < total; base += kPer * 1024) {
       int pid[kPer];
       uint32_t want[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = base + j * blockDim.x + threadIdx.x;
-        pid[j] = i < n ? bt[i] : 0;
-        want[j] = (i < n && ex) ? ex[i] : 0u;
+        const int i = base + j * 1024 + tid;
+        pid[j] = 0;
+        want[j] = 0u;
+        if (i < total) {
+          int u = 0;
+          while (s_off[u + 1] <= i) ++u;          // the unit holding flat entry i
+          const int row = a.head_layout ? b * a.num_kv_heads + u0 + u : b;
+          const size_t e = (size_t)row * a.table_width + (i - s_off[u]);
+          pid[j] = a.block_table[e];
+          if (a.expected_tags) want[j] = a.expected_tags[e];
+        }
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = base + j * blockDim.x + threadIdx.x;
-        if (i >= n) continue;
+        if (base + j * 1024 + tid >= total) continue;
         if ((unsigned)pid[j] >= (unsigned)a.num_pages) {
           bits |= 2u;
-        } else if (ex && want[j] != a.page_tags[pid[j]]) {
+        } else if (a.expected_tags && want[j] != a.page_tags[pid[j]]) {
           bits |= 1u;
         }
       }
     }
+    __syncthreads();   // s_off is rewritten by the next group of units
   }
   if (bits) atomicOr(&s_bits, bits);  // LDS atomic
   __syncthreads();
-  if (threadIdx.x == 0) a.flags[b] = s_bits;
+  if (tid == 0) a.flags[b] = s_bits;
+}
+
+// ----------------------------------------------------------------- plan
+// Length-balanced split of the automatic decode: one chunk size for the whole
+// batch, chosen from the real lengths, and group g (a sequence, or a unit in
+// the HEAD layout) gets ceil(pages_g / chunk) partitions of its pages.  The
+// chunk is the smallest (at least min_chunk) for which the partitions, each
+// last one of a group rounded up, make at most target_waves waves: every
+// wave then has at most `chunk` pages, and no compute unit holds more waves
+// than the rest.  With fixed partitions a ragged batch leaves only its
+// longest units' waves running at the end (measured: 56-72% of 8 TB/s against
+// 82-85% for the same kernels on uniform lengths), and a wave count just
+// above target_waves leaves a few compute units with a third wave per SIMD.
+// One workgroup; the partition counts are then scanned 1024 groups at a time.
+__device__ inline int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+constexpr int kPlanCache = 4096;   // groups whose page counts the planner keeps in LDS
+
+__device__ void plan_block(const PlanArgs& a) {
+  __shared__ int s_np[kPlanCache];
+  __shared__ long long s_part[2][16];
+  __shared__ int s_wave[16];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a.num_groups;
+  const int cap = a.table_width * kPageSize;
+  auto pages = [&](int g) {
+    int L = a.lens[g];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    return (L + kPageSize - 1) / kPageSize;
+  };
+  for (int g = tid; g < n && g < kPlanCache; g += 1024) s_np[g] = pages(g);
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  auto np_of = [&](int g) { return g < kPlanCache ? s_np[g] : pages(g); };
+  // block-wide sum of f(group); double-buffered, one barrier per call
+  int buf = 0;
+  auto block_sum = [&](auto f) {
+    long long v = 0;
+    for (int g = tid; g < n; g += 1024) v += f(np_of(g));
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
+    if (lane == 0) s_part[buf][wv] = v;
+    __syncthreads();
+    long long t = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += s_part[buf][i];
+    buf ^= 1;
+    return t;
+  };
+  const long long total = block_sum([](int p) { return p; });   // pages of all groups
+  const long long hpg = a.heads_per_group, target = a.target_waves, W = a.table_width;
+  // The smallest chunk in [lo, hi] whose waves fit the target, where lo is
+  // the bound from the page total alone and hi fits for sure: pairs <=
+  // total / c + groups, so hi = ceil(total / (target / hpg - groups)) (or
+  // the whole table).  Each pass, wave w tests candidate lo + (hi - lo) * w / 16
+  // on its own (lanes stride over the groups, sums saturate above the
+  // target) and the range shrinks to the gap below the first one that fits.
+  long long lo = (total * hpg + target - 1) / target;
+  if (lo < a.min_chunk) lo = a.min_chunk;
+  if (lo > W) lo = W;
+  const long long room = target / hpg - n;
+  long long hi = room > 0 ? (total + room - 1) / room : W;
+  if (hi > W) hi = W;
+  if (hi < lo) hi = lo;
+  const int cap_sum = (int)(target / hpg) + 1;   // pairs above this already fail
+  while (lo < hi) {                               // uniform loop: invariant hi fits (or is W)
+    const int c = (int)(lo + (hi - lo) * wv / 16);
+    int v = 0;
+    for (int g = lane; g < n && v < cap_sum; g += 64) v += (np_of(g) + c - 1) / c;
+    v = min(v, cap_sum);
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
+    if (lane == 0) s_part[buf][wv] = (long long)v * hpg <= target ? 1 : 0;
+    __syncthreads();
+    int w = 0;
+    while (w < 16 && s_part[buf][w] == 0) ++w;
+    buf ^= 1;
+    if (w == 0) {
+      hi = lo;
+    } else {
+      const long long below = lo + (hi - lo) * (w - 1) / 16;   // candidate w - 1 fails
+      if (w < 16) hi = lo + (hi - lo) * w / 16;
+      lo = below + 1;
+    }
+  }
+  const int chunk = (int)hi;
+  int32_t* first = a.plan + 2;
+  for (int base = 0; base < n; base += 1024) {
+    const int g = base + tid;
+    const int parts = g < n ? (np_of(g) + chunk - 1) / chunk : 0;
+    const int incl = wave_incl_scan(parts, lane);
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+      const int x = lane < 16 ? s_wave[lane] : 0;
+      const int xi = wave_incl_scan(x, lane);
+      if (lane < 16) s_wave[lane] = xi - x;
+    }
+    __syncthreads();
+    const int excl = s_carry + s_wave[wv] + incl - parts;
+    if (g < n) {
+      first[g] = excl;
+      for (int p = 0; p < parts && excl + p < a.max_pairs; ++p) a.plan_group[excl + p] = g;
+    }
+    __syncthreads();
+    if (tid == 1023) s_carry = excl + parts;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.plan[0] = chunk;
+    a.plan[1] = min(s_carry, a.max_pairs);   // never clipped: max_pairs bounds the count
+    first[n] = s_carry;
+  }
+}
+
+// The validation and the plan share one launch: workgroups 0 .. nval - 1
+// validate sequences, and one more (when a plan is asked for) plans; the plan
+// reads only the lengths, so it runs beside the validation.
+__global__ __launch_bounds__(1024) void prep_kernel(ValidateArgs v, PlanArgs p, int nval) {
+  if ((int)blockIdx.x < nval) validate_block(v, blockIdx.x);
+  else plan_block(p);
 }
 
 // ------------------------------------------------------------- attention
@@ -171,8 +320,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   __shared__ bf16x8 s_q[QLDS ? kWaves : 1][QLDS ? NQ * NSTEP : 1][64];
 
   const int Pn = a.num_parts;
-  const int ppw = NQ == 1 ? a.parts_per_wave : 1;
-  const int groups = (Pn + ppw - 1) / ppw;     // waves per unit
+  const bool planned = a.plan != nullptr;      // length-balanced split (see plan_kernel)
+  const int ppw = (NQ == 1 && !planned) ? a.parts_per_wave : 1;
+  const int groups = (Pn + ppw - 1) / ppw;     // waves per unit (fixed partitions)
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   const int T = CAUSAL ? a.q_len : 1;
   const int C = G * T;                         // query columns of the unit
@@ -183,7 +333,34 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // per-page index, bound and branch in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int b, h, g, cb = 0;  // sequence, KV head, partition group, column block of this wave
-  if (a.xcd_order) {
+  int chunk = a.chunk_pages;
+  bool direct = Pn == 1;   // no reduce follows for this wave's unit: it writes the output rows
+  int pslot = 0;           // planned: this wave's partial slot
+  if (planned) {
+    // One partition per pair, all of about the same size; the workgroup
+    // order (XCD-aware for SEQ, as below) is the same, over the plan's pairs.
+    const int hpg = HEAD ? 1 : Hkv;
+    int pair, hh;
+    if (a.xcd_order) {
+      const int hgs = Hkv / kWaves;
+      const int x = blockIdx.x;
+      pair = (x / (8 * hgs)) * 8 + (x % 8);
+      hh = ((x / 8) % hgs) * kWaves + wave;
+    } else {
+      const int item = blockIdx.x * kWaves + wave;
+      pair = item / hpg;
+      hh = item - pair * hpg;
+    }
+    if (pair >= a.plan[1]) return;
+    chunk = a.plan[0];
+    const int grp = a.plan_group[pair];
+    const int first = a.plan[2 + grp];
+    g = pair - first;
+    direct = a.plan[3 + grp] - first == 1;
+    b = HEAD ? grp / Hkv : grp;
+    h = HEAD ? grp - b * Hkv : hh;
+    pslot = pair * hpg + hh;
+  } else if (a.xcd_order) {
     // Workgroups are dealt to the 8 XCDs in turn (id % 8).  A workgroup holds
     // 4 heads of one (sequence, partition group) pair, and the Hkv/4
     // workgroups of a pair get ids 8 apart -- same XCD, launched together --
@@ -227,8 +404,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     const int seen = L - T + (cend - 1) / G + 1;
     npages = seen > 0 ? min(npages, (seen + kPageSize - 1) / kPageSize) : 0;
   }
-  const int p0 = part0 * a.chunk_pages;
-  const int p1 = min(min(part0 + ppw, Pn) * a.chunk_pages, npages);
+  const int p0 = part0 * chunk;
+  const int p1 = planned ? min(p0 + chunk, npages) : min(min(part0 + ppw, Pn) * chunk, npages);
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
   // query row (in [B][T][Hq]) of column cc of this unit
   auto col_row = [&](int cc) {
@@ -236,7 +413,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     return ((size_t)b * T + t) * Hq + h * G + (cc - t * G);
   };
   if (flagged || p0 >= p1) {
-    if (Pn == 1) {  // no reduce follows: this wave owns the output rows
+    if (direct) {
       for (int i = lane; i < (cend - cbase) * D; i += 64)
         a.out[col_row(cbase + i / D) * D + i % D] = 0;
     }
@@ -480,7 +657,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       const int cc = cbase + 16 * nq + c;
       if (cc < cend) {
         const size_t qrow = col_row(cc);
-        if (Pn == 1) {
+        if (direct) {
           if (a.row_ml != nullptr && q4 == 0) {   // scored decode: the row's final (max, sum)
             a.row_ml[qrow * 2 + 0] = m_run[nq];
             a.row_ml[qrow * 2 + 1] = l_tot;
@@ -494,12 +671,14 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
           }
         } else {
-          float* po = a.part_o + (qrow * Pn + part) * D;
+          // fixed partitions: [row][Pn]; planned: [slot][column]
+          const size_t pi = planned ? (size_t)pslot * C + cc : qrow * Pn + part;
+          float* po = a.part_o + pi * D;
 #pragma unroll
           for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = o[nq][j];
           if (q4 == 0) {
-            a.part_ml[(qrow * Pn + part) * 2 + 0] = m_run[nq];
-            a.part_ml[(qrow * Pn + part) * 2 + 1] = l_tot;
+            a.part_ml[pi * 2 + 0] = m_run[nq];
+            a.part_ml[pi * 2 + 1] = l_tot;
           }
         }
       }
@@ -514,7 +693,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   u32x4 kr[PIPE][NSEG], vr[PIPE][NSEG];
   float ks[PIPE], vs[PIPE];
   int part = part0;
-  int next_boundary = a.chunk_pages;  // page index (relative to p0) of the next partition
+  int next_boundary = chunk;  // page index (relative to p0) of the next partition
   float (*stash)[64] = s_stash[wave];
   for (int seg = 0; seg < n; seg += kSegPages) {
     const int m = min(kSegPages, n - seg);
@@ -566,7 +745,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
               stash[4 * NT][lane] = m_run[0];
               stash[4 * NT + 1][lane] = l_acc[0];
               ++part;
-              next_boundary += a.chunk_pages;
+              next_boundary += chunk;
 #pragma unroll
               for (int j = 0; j < NT; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
               m_run[0] = -INFINITY;
@@ -595,7 +774,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 // ---------------------------------------------------------------- reduce
 // One workgroup per query row (sequence, query token, query head); thread d
 // merges dim d over the partitions that hold tokens visible to the row, in
-// partition order (deterministic).
+// partition order (deterministic).  With the length-balanced split, rows of
+// single-partition units were written by the attention kernel and are left
+// alone.
 template <int D, bool HEAD>
 __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   const int qrow = blockIdx.x;
@@ -613,15 +794,29 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int vis = L - T + t + 1;   // tokens this row sees (T = 1: all L)
   const int npages = vis > 0 ? (vis + kPageSize - 1) / kPageSize : 0;
-  const int nvp = (npages + a.chunk_pages - 1) / a.chunk_pages;
+  // partials of this row: fixed partitions [row][Pn]; planned [slot][column],
+  // slots first * hpg + h_in_group, stepping by hpg per partition
+  int chunk = a.chunk_pages, nparts = a.num_parts;
+  size_t pi0 = (size_t)qrow * nparts, step = 1;
+  if (a.plan != nullptr) {
+    const int hpg = HEAD ? 1 : a.num_kv_heads;
+    const int grp = HEAD ? row : b;
+    const int first = a.plan[2 + grp];
+    chunk = a.plan[0];
+    nparts = a.plan[3 + grp] - first;
+    const int C = a.group * T;
+    pi0 = ((size_t)first * hpg + (HEAD ? 0 : h)) * C + t * a.group + (hq - h * a.group);
+    step = (size_t)hpg * C;
+  }
+  const int nvp = min(nparts, (npages + chunk - 1) / chunk);
   const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
   if (flagged || nvp == 0) {
     a.out[(size_t)qrow * D + d] = 0;
     return;
   }
-  const int Pn = a.num_parts;
-  const float* ml = a.part_ml + (size_t)qrow * Pn * 2;
-  const float* po = a.part_o + (size_t)qrow * Pn * D + d;
+  if (a.plan != nullptr && nparts == 1) return;   // written by the attention kernel
+  const float* ml = a.part_ml + pi0 * 2;
+  const float* po = a.part_o + pi0 * D + d;
   // Partitions in groups of 8, every load of a group issued before use; a
   // running (max, sum, O) merges the groups in partition order.
   constexpr int kGrp = 8;
@@ -631,9 +826,9 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < kGrp; ++j) {
       const bool ok = p0 + j < nvp;
-      m[j] = ok ? ml[2 * (p0 + j)] : -INFINITY;
-      l[j] = ok ? ml[2 * (p0 + j) + 1] : 0.f;
-      o[j] = ok ? po[(size_t)(p0 + j) * D] : 0.f;
+      m[j] = ok ? ml[2 * step * (p0 + j)] : -INFINITY;
+      l[j] = ok ? ml[2 * step * (p0 + j) + 1] : 0.f;
+      o[j] = ok ? po[step * (p0 + j) * D] : 0.f;
     }
     float Mg = M;
 #pragma unroll
@@ -658,15 +853,21 @@ __global__ __launch_bounds__(D) void reduce_kernel(AttnArgs a) {
 
 template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  const int ppw = NQ == 1 ? a.parts_per_wave : 1;
-  const unsigned groups = (unsigned)(a.num_parts + ppw - 1) / ppw;
   unsigned grid;
-  if (a.xcd_order) {  // see attention_kernel: (Hkv / 4) workgroups per pair, in blocks of 8 pairs
-    const unsigned pairs = (unsigned)a.batch * groups;
-    grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
+  if (a.plan != nullptr) {  // enough waves for the most pairs a plan can hold; the rest exit
+    const unsigned pairs = (unsigned)a.max_pairs;
+    if (a.xcd_order) grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
+    else grid = (pairs * (HEAD ? 1u : (unsigned)a.num_kv_heads) + kWaves - 1) / kWaves;
   } else {
-    const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.col_blocks * groups;
-    grid = (items + kWaves - 1) / kWaves;
+    const int ppw = NQ == 1 ? a.parts_per_wave : 1;
+    const unsigned groups = (unsigned)(a.num_parts + ppw - 1) / ppw;
+    if (a.xcd_order) {  // see attention_kernel: (Hkv / 4) workgroups per pair, in blocks of 8 pairs
+      const unsigned pairs = (unsigned)a.batch * groups;
+      grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
+    } else {
+      const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.col_blocks * groups;
+      grid = (items + kWaves - 1) / kWaves;
+    }
   }
   hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL>), dim3(grid),
                      dim3(64 * kWaves), 0, s, a);
@@ -900,8 +1101,12 @@ hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_validate(const ValidateArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(validate_kernel, dim3(a.batch), dim3(256), 0, s, a);
+hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p, hipStream_t s) {
+  const int nval = v ? v->batch : 0;
+  const unsigned grid = (unsigned)nval + (p ? 1u : 0u);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(1024), 0, s, v ? *v : ValidateArgs{},
+                     p ? *p : PlanArgs{}, nval);
   return hipGetLastError();
 }
 

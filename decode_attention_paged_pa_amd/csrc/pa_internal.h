@@ -35,6 +35,25 @@ struct AttnArgs {
   int parts_per_wave;        // consecutive partitions of one unit a wave streams through
   int xcd_order;             // workgroup order that keeps a page's heads on one XCD
   float score_scale_log2;    // softmax_scale * log2(e)
+  // Length-balanced split (automatic partitions; nullptr: fixed partitions of
+  // chunk_pages).  Written by plan_kernel: plan[0] the chunk in pages,
+  // plan[1] the number of pairs, plan[2 + g] the first pair of group g
+  // (groups + 1 entries); plan_group[pair] the group of each pair.  A group
+  // is a sequence (SEQ: its Hkv heads share the pair) or a unit (HEAD); a
+  // pair is one partition of a group, and its partials sit in slots
+  // pair * heads_per_group + head.
+  const int32_t* plan;
+  const int32_t* plan_group;
+  int max_pairs;
+};
+
+// Arguments of the length-balanced split planner.
+struct PlanArgs {
+  const int32_t* lens;       // one length per group
+  int32_t* plan;             // as AttnArgs::plan
+  int32_t* plan_group;
+  int num_groups, heads_per_group, table_width, max_pairs;
+  int target_waves, min_chunk;
 };
 
 struct ValidateArgs {
@@ -101,7 +120,9 @@ __host__ __device__ inline size_t v_block_slot(int pid, int h, int num_kv_heads,
   return head_layout ? (size_t)p : (size_t)p * num_kv_heads + h;
 }
 
-hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+// Validation of v->batch sequences (v may be null) and the split plan (p may
+// be null), in one launch.
+hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,
                             hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);

@@ -246,6 +246,8 @@ def workspace_bytes(cache, block_table, lens, num_q_heads, num_partitions=0):
 
 
 def num_partitions(cache, block_table, lens, num_q_heads, num_partitions=0):
+    """pa_decode_num_partitions: the count given, 1 for automatic on tables of at
+    most 32 pages, else 0 (automatic: balanced on the device from the lengths)."""
     sd = _seq(cache, block_table, lens)
     cd = cache.desc()
     n = lib().pa_decode_num_partitions(ctypes.byref(cd), ctypes.byref(sd), num_q_heads,

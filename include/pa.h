@@ -167,12 +167,20 @@ int pa_cache_append(const pa_cache_desc *cache, const pa_seq_desc *seq, const in
  * Bytes of device workspace pa_decode needs for this shape and partition
  * count (0 = the library's choice).  0 when the decode needs none (one
  * partition per unit).  Returns (size_t)-1 for invalid arguments.
+ * With the automatic, length-balanced split (num_partitions 0, table_width
+ * above 32) the size is the most any lengths can need: partials for
+ * ceil(2048 / h) + groups (group, partition) pairs, where a group is a
+ * sequence holding h = Hkv heads (SEQ) or one unit with h = 1 (HEAD), each
+ * head G columns of D + 2 floats, plus the split plan: (groups + 3) and
+ * (pairs) int32, every block rounded up to 256 bytes.
  */
 size_t pa_decode_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
                                  int32_t num_q_heads, int32_t num_partitions);
 
-/* Number of token partitions pa_decode will use for this shape (after the
- * automatic choice when num_partitions == 0); negative PA_ERR_* on error. */
+/* Number of token partitions pa_decode will use for this shape: the count
+ * given, or for num_partitions == 0 the library's choice: 1 for tables of at
+ * most 32 pages, else 0, which means balanced at run time (below).  Negative
+ * PA_ERR_* on error. */
 int pa_decode_num_partitions(const pa_cache_desc *cache, const pa_seq_desc *seq,
                              int32_t num_q_heads, int32_t num_partitions);
 
@@ -194,7 +202,13 @@ int pa_decode_num_partitions(const pa_cache_desc *cache, const pa_seq_desc *seq,
  * still never read outside the pool or past table_width.
  * Rows of flagged sequences and of units with no tokens are written as +0.0.
  *
- * num_partitions: split of each unit's tokens (split-K); 0 = automatic.
+ * num_partitions: split of each unit's tokens (split-K) into that many
+ * partitions of ceil(table_width / n) pages.  0 = automatic: for tables of
+ * more than 32 pages the split is balanced on the device from the real
+ * lengths -- one chunk size for the batch, about 2048 waves of equal work
+ * (at least 32 pages each), so a ragged batch keeps every compute unit
+ * streaming to the end.  The merge order then depends on the lengths; a
+ * given input always gives the same bits.
  * workspace: device buffer of at least pa_decode_workspace_bytes(...) bytes,
  * 256-byte aligned (may be NULL when that size is 0).
  */
@@ -204,8 +218,9 @@ int pa_decode(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_
 
 /*
  * pa_decode, plus timing events recorded on `stream` around its kernels:
- * events[0] before validation, events[1] before attention, events[2] after
- * attention, events[3] after the partition reduce.  Any entry may be NULL.
+ * events[0] before validation, events[1] before attention (after the split
+ * plan, when automatic), events[2] after attention, events[3] after the
+ * partition reduce.  Any entry may be NULL.
  */
 int pa_decode_timed(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
                     const uint16_t *q, uint16_t *out, float softmax_scale, int32_t num_partitions,

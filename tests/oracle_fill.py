@@ -32,14 +32,16 @@ def oracle_fill(w, seqs=None, cache=None):
         k_hist, v_hist, k_new, v_new, n_hist = w.seq_kv(b)
         kv[b] = (k_hist, v_hist, k_new, v_new, n_hist)
         bt, _ = seq_rows(w, b)
+        # the step appends q_len tokens to every unit that is not empty (an
+        # empty unit has neither history nor step tokens)
         if w.layout == "seq":
             zero = np.zeros(1, np.int32)
             n1 = np.array([n_hist[0]], np.int32)
-            one = np.full(1, w.q_len, np.int32)
+            one = np.full(1, w.q_len if int(w.lens[b]) > 0 else 0, np.int32)
         else:
             zero = np.zeros((1, w.Hkv), np.int32)
             n1 = n_hist[None, :].astype(np.int32)
-            one = np.full((1, w.Hkv), w.q_len, np.int32)
+            one = np.where(w.lens[b:b + 1] > 0, w.q_len, 0).astype(np.int32)
         f1 = oracle_append(cache, bt, zero, n1, k_hist[None], v_hist[None], w.W)
         f2 = oracle_append(cache, bt, n1, one, k_new[None], v_new[None], w.W)
         assert f1[0] == 0 and f2[0] == 0

@@ -129,10 +129,25 @@ def test_partition_choice():
     c = _cache()
     n = lambda s, p: L.pa_decode_num_partitions(ctypes.byref(c), ctypes.byref(s), 64, p)  # noqa: E731
     assert n(_seq(batch=64, table_width=2048), 8) == 8
-    assert n(_seq(batch=64, table_width=2048), 0) == 4     # auto: 512 pages per partition
+    assert n(_seq(batch=64, table_width=2048), 0) == 0     # auto: balanced at run time
     assert n(_seq(batch=4, table_width=32), 0) == 1        # tiny: one partition, no reduce
     assert n(_seq(batch=4, table_width=32), 3) == 3
     assert L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(_seq(table_width=32)), 64, 1) == 0
+    assert L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(_seq(table_width=32)), 64, 0) == 0
+    # balanced split: at most ceil(2048 / heads per pair) + groups pairs; per pair and head
+    # G * T columns of D floats and (max, sum); then the plan (groups + 3 ints) and the
+    # group of each pair, every block 256-byte aligned
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ws = lambda cc, ss, hq=64: L.pa_decode_workspace_bytes(ctypes.byref(cc), ctypes.byref(ss), hq, 0)  # noqa: E731
+    pairs = 2048 // 8 + 64                                  # SEQ: a pair holds the 8 heads of a sequence
+    slots = pairs * 8 * 8
+    assert ws(c, _seq(batch=64, table_width=2048)) == (
+        a256(slots * 128 * 4) + a256(slots * 8) + a256((64 + 3) * 4) + a256(pairs * 4))
+    ch = _cache(layout=1)                                   # HEAD: a pair is one unit's partition
+    pairs = 2048 + 16 * 8
+    slots = pairs * 4
+    assert ws(ch, _seq(batch=16, table_width=2048), hq=32) == (
+        a256(slots * 128 * 4) + a256(slots * 8) + a256((16 * 8 + 3) * 4) + a256(pairs * 4))
 
 
 def _decode_multi(cache, seq, hq=32, q_len=4, q=FAKE, out=FAKE, scale=0.088, parts=0, flags=None,
