@@ -377,6 +377,25 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     g = pair / a.batch;
     b = pair - g * a.batch;
     h = hg * kWaves + wave;
+  } else if (cblocks > 1) {
+    // Prefill: every column block of a unit reads the same pages, so all of
+    // a unit's waves go to one XCD (workgroups are dealt to the 8 XCDs in
+    // turn, id % 8), where they walk its pages together through one L2.
+    // Dealt across XCDs instead, each L2 saw every unit and hit 43% of its
+    // requests (measured on the 2048-token chunk).  Within a unit the blocks
+    // that see the most pages start first.
+    const int per = cblocks * groups;               // waves of one unit
+    const int wgu = (per + kWaves - 1) / kWaves;    // workgroups of one unit
+    const int x = blockIdx.x;
+    const int k = x >> 3;
+    const int unit = (k / wgu) * 8 + (x & 7);
+    const int j = (k - (k / wgu) * wgu) * kWaves + wave;   // wave within the unit
+    if (unit >= a.batch * Hkv || j >= per) return;
+    const int jb = j / groups;
+    g = j - jb * groups;
+    cb = cblocks - 1 - jb;
+    b = unit / Hkv;
+    h = unit - b * Hkv;
   } else {
     const int item = blockIdx.x * kWaves + wave;
     if (item >= a.batch * Hkv * cblocks * groups) return;
@@ -864,6 +883,10 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     if (a.xcd_order) {  // see attention_kernel: (Hkv / 4) workgroups per pair, in blocks of 8 pairs
       const unsigned pairs = (unsigned)a.batch * groups;
       grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
+    } else if (a.col_blocks > 1) {  // see attention_kernel: a unit's workgroups on one XCD
+      const unsigned wgu = ((unsigned)a.col_blocks * groups + kWaves - 1) / kWaves;
+      const unsigned units = (unsigned)a.batch * a.num_kv_heads;
+      grid = ((units + 7) / 8) * 8 * wgu;
     } else {
       const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.col_blocks * groups;
       grid = (items + kWaves - 1) / kWaves;
