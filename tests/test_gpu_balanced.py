@@ -110,3 +110,31 @@ def test_scored_balanced_matches_fixed_split():
         got[p] = scores.cpu().numpy().astype(np.float64)
     d = np.abs(got[0] - got[4])
     assert np.all(d <= 1e-5 * np.abs(got[4]) + 1e-12), d.max()
+
+
+def test_graph_replans_when_lengths_change():
+    """A captured decode step reads the lengths at every replay, so the split
+    is planned anew: after the lengths change in place, a replay equals the
+    eager decode of the same cache, bit for bit."""
+    w = make_workload(2, batch=4, lens=[50, 600, 1500, 3000], stale_frac=0.0)
+    dw = build_device_workload(w)
+    dw.step_append()
+    g = pa.DecodeStepGraph(dw.cache, dw.block_table, dw.lens_old, dw.n_step, dw.k_step, dw.v_step,
+                           dw.q, dw.lens, w.sigma, expected_tags=dw.expected_tags, flags=dw.flags)
+    first = g.replay().clone()
+    torch.cuda.synchronize()
+    ref = dw.decode(check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), ref.view(torch.int16))
+    # long sequences get short, a short one grows within its last page (the
+    # table holds pages for the old lengths only)
+    new = torch.tensor([60, 200, 1500, 100], dtype=torch.int32, device="cuda")
+    dw.lens.copy_(new)
+    dw.lens_old.copy_(new - 1)
+    out = g.replay().clone()             # appends at the new positions, then decodes
+    torch.cuda.synchronize()
+    ref = dw.decode(check=True)
+    torch.cuda.synchronize()
+    assert np.all(flags_of(dw) == 0)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert not torch.equal(out[3].view(torch.int16), first[3].view(torch.int16))
