@@ -271,9 +271,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=5, help="workload 2..5")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload: 2 llama8b-bf16, 3 llama8b-fp8-tags, 4 headwise-bf16, "
+                         "5 70b-fp8-32k (B 64, 64/8 heads, D 128, 32K tokens, FP8)")
     ap.add_argument("--partitions", type=int, default=-1,
-                    help="split-K count (-1: 8 for workload 5 decode, else the library's choice)")
+                    help="split-K count (-1: 8 for the 70b-fp8-32k decode, else the library's "
+                         "choice)")
     ap.add_argument("--no-check", action="store_true", help="no-op tracker: skip the tag check")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's timed sample")
@@ -292,7 +295,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
