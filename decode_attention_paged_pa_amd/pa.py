@@ -5,8 +5,14 @@ checks tensor dtypes, shapes and devices, passes raw device pointers and the
 current HIP stream, and turns negative return codes into exceptions.  It has
 no CPU fallback: without the built library every call raises.
 
-Entry points mirror include/pa.h: append (pa_cache_append), decode
-(pa_decode / pa_decode_timed), workspace_bytes, num_partitions, pool_bytes.
+Entry points mirror include/pa.h: append (pa_cache_append); decode
+(pa_decode / pa_decode_timed), workspace_bytes, num_partitions; decode_multi
+(pa_decode_multi: causal drafts), multi_workspace_bytes; decode_scored
+(pa_decode_scored: eviction scores), scored_workspace_bytes; compact
+(pa_cache_compact); prefill (pa_prefill), prefill_workspace_bytes,
+prefill_num_partitions; version.  PagedKVCache owns the pools, scales and tags
+(sized by pa_pool_bytes); DecodeStepGraph captures append + decode as one HIP
+graph.
 """
 import ctypes
 import os
