@@ -137,8 +137,11 @@ Split prefill_split(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, in
 // Pn > 1; planned, [pair][head in group][T * G columns] plus the plan
 // (int32: chunk, pair count, groups + 1 first pairs, the group of each pair).
 // A scored decode also keeps the rows' final (max, sum) [B][Hq][2].
+Split mass_split(const pa_cache_desc* c, const pa_seq_desc* s);
+
 struct WorkspaceLayout {
-  size_t part_o = 0, part_ml = 0, plan = 0, plan_group = 0, row_ml = 0, total = 0;
+  size_t part_o = 0, part_ml = 0, plan = 0, plan_group = 0, row_ml = 0;
+  size_t mass_plan = 0, mass_group = 0, total = 0;
 };
 
 WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
@@ -165,6 +168,11 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, i
   if (scored) {
     w.row_ml = off;
     off += align256((size_t)s->batch * hq * 2 * sizeof(float));
+    const Split ms = mass_split(c, s);
+    w.mass_plan = off;
+    off += align256(((size_t)ms.groups + 3) * sizeof(int32_t));
+    w.mass_group = off;
+    off += align256((size_t)ms.max_pairs * sizeof(int32_t));
   }
   w.total = off;
   return w;
@@ -175,26 +183,27 @@ size_t workspace_for(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, i
   return workspace_layout(c, s, hq, q_len, sp, scored).total;
 }
 
-// Eviction score pass: K-only streaming, one wave per run of pages; runs of
-// 16 to kMassRun pages (the wave's LDS rows), enough of them for about
-// kMassTargetWaves waves.
+// Eviction score pass: K-only streaming, one wave per run of 16 to kMassRun
+// pages (the wave's LDS rows), from a length-balanced plan of its own aiming
+// at kMassPlanWaves waves.
 #ifndef PA_MASS_WAVES
 #define PA_MASS_WAVES 4096
 #endif
-constexpr int64_t kMassTargetWaves = PA_MASS_WAVES;
+constexpr int kMassPlanWaves = PA_MASS_WAVES;
+constexpr int kMassMinChunk = 16;
 
-void choose_mass_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int* chunk_pages,
-                            int* num_parts) {
-  const int W = s->table_width;
-  const int64_t units = (int64_t)s->batch * c->num_kv_heads;
-  int64_t p = (kMassTargetWaves + units - 1) / units;
-  const int64_t pmin = (W + pa::kMassRun - 1) / pa::kMassRun;
-  const int64_t pmax = (W + 15) / 16;
-  p = p > pmax ? pmax : p;
-  p = p < pmin ? pmin : p;
-  const int cp = (int)((W + p - 1) / p);
-  *chunk_pages = cp;
-  *num_parts = (W + cp - 1) / cp;
+Split mass_split(const pa_cache_desc* c, const pa_seq_desc* s) {
+  Split sp;
+  const bool head = c->layout == PA_LAYOUT_HEAD;
+  sp.planned = true;
+  sp.hpg = head ? 1 : c->num_kv_heads;
+  sp.groups = head ? s->batch * c->num_kv_heads : s->batch;
+  // a fitting chunk gives at most target / hpg + groups pairs; the cap
+  // (kMassRun pages) at most ceil(W / kMassRun) per group
+  const int64_t fit = (kMassPlanWaves + sp.hpg - 1) / sp.hpg + sp.groups;
+  const int64_t capped = (int64_t)sp.groups * ((s->table_width + pa::kMassRun - 1) / pa::kMassRun);
+  sp.max_pairs = (int)(fit > capped ? fit : capped);
+  return sp;
 }
 
 // Chunked prefill: a unit's G * T query columns go in blocks of 64, one wave
@@ -289,8 +298,24 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
     pl.max_pairs = sp.max_pairs;
     pl.target_waves = (int)kPlanWaves;
     pl.min_chunk = kPlanMinChunk;
+    pl.max_chunk = seq->table_width;
   }
-  if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, stream) != hipSuccess)
+  pa::PlanArgs pm{};
+  const Split ms = scores ? mass_split(cache, seq) : Split{};
+  if (scores) {
+    pm.lens = seq->lens;
+    pm.plan = reinterpret_cast<int32_t*>(ws + wl.mass_plan);
+    pm.plan_group = reinterpret_cast<int32_t*>(ws + wl.mass_group);
+    pm.num_groups = ms.groups;
+    pm.heads_per_group = ms.hpg;
+    pm.table_width = seq->table_width;
+    pm.max_pairs = ms.max_pairs;
+    pm.target_waves = kMassPlanWaves;
+    pm.min_chunk = kMassMinChunk;
+    pm.max_chunk = pa::kMassRun;
+  }
+  if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, scores ? &pm : nullptr,
+                      stream) != hipSuccess)
     return PA_ERR_LAUNCH;
   rec(1);
 
@@ -343,9 +368,9 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (scores) {   // second pass: K again, with the rows' final (max, sum)
     pa::AttnArgs m = a;
     m.scores = scores;
-    m.plan = nullptr;
-    m.plan_group = nullptr;
-    choose_mass_partitions(cache, seq, &m.chunk_pages, &m.num_parts);
+    m.plan = reinterpret_cast<const int32_t*>(ws + wl.mass_plan);
+    m.plan_group = reinterpret_cast<const int32_t*>(ws + wl.mass_group);
+    m.max_pairs = ms.max_pairs;
     if (pa::launch_mass(m, cache->head_dim, fp8, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   rec(3);

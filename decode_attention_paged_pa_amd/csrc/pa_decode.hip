@@ -209,7 +209,8 @@ __device__ void plan_block(const PlanArgs& a) {
     return t;
   };
   const long long total = block_sum([](int p) { return p; });   // pages of all groups
-  const long long hpg = a.heads_per_group, target = a.target_waves, W = a.table_width;
+  const long long hpg = a.heads_per_group, target = a.target_waves;
+  const long long W = min(a.max_chunk, a.table_width);   // the largest chunk allowed
   // The smallest chunk in [lo, hi] whose waves fit the target, where lo is
   // the bound from the page total alone and hi fits for sure: pairs <=
   // total / c + groups, so hi = ceil(total / (target / hpg - groups)) (or
@@ -274,12 +275,15 @@ __device__ void plan_block(const PlanArgs& a) {
   }
 }
 
-// The validation and the plan share one launch: workgroups 0 .. nval - 1
-// validate sequences, and one more (when a plan is asked for) plans; the plan
-// reads only the lengths, so it runs beside the validation.
-__global__ __launch_bounds__(1024) void prep_kernel(ValidateArgs v, PlanArgs p, int nval) {
-  if ((int)blockIdx.x < nval) validate_block(v, blockIdx.x);
-  else plan_block(p);
+// The validation and the plans share one launch: workgroups 0 .. nval - 1
+// validate sequences, and one more per plan asked for (the decode's split,
+// the score pass's split) plans; the plans read only the lengths, so they run
+// beside the validation.
+__global__ __launch_bounds__(1024) void prep_kernel(ValidateArgs v, PlanArgs p0, PlanArgs p1,
+                                                    int nval) {
+  const int x = blockIdx.x;
+  if (x < nval) validate_block(v, x);
+  else plan_block(x == nval ? p0 : p1);
 }
 
 // ------------------------------------------------------------- attention
@@ -922,8 +926,12 @@ hipError_t launch_attention_q(const AttnArgs& a, hipStream_t s) {
 // per page and head each way, a write stream that measured about 45% of the
 // decode kernel's time when it ran inside it.
 //
-// One wave per (unit, run of chunk_pages <= 128 pages), heads fastest, so a
-// workgroup's four waves read neighbouring head blocks of the same pages.
+// One wave per (unit, run of at most 128 pages).  The runs come from a
+// length-balanced plan of their own (plan_block; chunk between 16 and 128
+// pages, about 4096 waves of equal work): with runs of a fixed length a
+// ragged batch left few waves running at the end.  A SEQ pair's heads are
+// neighbouring waves, so a workgroup reads neighbouring head blocks of the
+// same pages.
 // Lane (c, q4) owns query head c and tokens 4*q4 .. 4*q4+3 of each page; the
 // sum over heads is a butterfly across the 16 lanes of a DPP row (fixed
 // order: deterministic).  The page's 16 sums go to the wave's own LDS rows,
@@ -958,12 +966,17 @@ __global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
   constexpr int PIPE = PA_MASS_PIPE;
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Runs from the score pass's own length-balanced plan (chunk <= kMassRun
+  // pages), heads of a SEQ pair in neighbouring waves.
+  const int hpg = HEAD ? 1 : Hkv;
   const int item = blockIdx.x * kWaves + wave;
-  if (item >= a.batch * Hkv * a.num_parts) return;
-  const int h = item % Hkv;
-  const int rest = item / Hkv;
-  const int b = rest % a.batch;
-  const int part = rest / a.batch;
+  const int pair = item / hpg;
+  if (pair >= a.plan[1]) return;
+  const int chunk = a.plan[0];
+  const int grp = a.plan_group[pair];
+  const int part = pair - a.plan[2 + grp];
+  const int b = HEAD ? grp / Hkv : grp;
+  const int h = HEAD ? grp - b * Hkv : item - pair * hpg;
   if (a.flags != nullptr && a.flags[b] != 0u) return;   // aborted request: no update
   const int unit = b * Hkv + h;
   const int row = HEAD ? unit : b;
@@ -971,10 +984,10 @@ __global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
   int L = a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int npages = (L + kPageSize - 1) / kPageSize;
-  const int p0 = part * a.chunk_pages;
-  const int p1 = min(p0 + a.chunk_pages, npages);
+  const int p0 = part * chunk;
+  const int p1 = min(p0 + chunk, npages);
   if (p0 >= p1) return;
-  const int n = min(p1 - p0, kMassRun);   // the host's runs are never longer
+  const int n = min(p1 - p0, kMassRun);   // the plan's runs are never longer
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, q4 = lane >> 4;
   const bool col = c < G;
@@ -1116,7 +1129,7 @@ __global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
 
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
-  const unsigned items = (unsigned)a.batch * a.num_kv_heads * a.num_parts;
+  const unsigned items = (unsigned)a.max_pairs * (HEAD ? 1u : (unsigned)a.num_kv_heads);
   hipLaunchKernelGGL((mass_kernel<D, FP8, HEAD>), dim3((items + kWaves - 1) / kWaves),
                      dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
@@ -1124,12 +1137,14 @@ hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p, hipStream_t s) {
+hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p0, const PlanArgs* p1,
+                       hipStream_t s) {
+  if (!p0 && p1) return launch_prep(v, p1, nullptr, s);
   const int nval = v ? v->batch : 0;
-  const unsigned grid = (unsigned)nval + (p ? 1u : 0u);
+  const unsigned grid = (unsigned)nval + (p0 ? 1u : 0u) + (p1 ? 1u : 0u);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(1024), 0, s, v ? *v : ValidateArgs{},
-                     p ? *p : PlanArgs{}, nval);
+                     p0 ? *p0 : PlanArgs{}, p1 ? *p1 : PlanArgs{}, nval);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ struct PlanArgs {
   int32_t* plan;             // as AttnArgs::plan
   int32_t* plan_group;
   int num_groups, heads_per_group, table_width, max_pairs;
-  int target_waves, min_chunk;
+  int target_waves, min_chunk, max_chunk;
 };
 
 struct ValidateArgs {
@@ -120,9 +120,10 @@ __host__ __device__ inline size_t v_block_slot(int pid, int h, int num_kv_heads,
   return head_layout ? (size_t)p : (size_t)p * num_kv_heads + h;
 }
 
-// Validation of v->batch sequences (v may be null) and the split plan (p may
-// be null), in one launch.
-hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p, hipStream_t s);
+// Validation of v->batch sequences (v may be null) and up to two split plans
+// (p0, p1 may be null), in one launch.
+hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p0, const PlanArgs* p1,
+                       hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,
                             hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);

@@ -190,8 +190,12 @@ def test_decode_scored_arguments_and_workspace():
     assert sc(scores=0) == -1
     assert sc(scores=FAKE + 2) == -1
     need1 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 1)
-    # the rows' final (max, sum) [B][Hq][2] fp32; no partials at Pn = 1
-    assert need1 == 4 * 32 * 2 * 4
+    # the rows' final (max, sum) [B][Hq][2] fp32 (no partials at Pn = 1), then the score
+    # pass's plan: (groups + 3) int32 and its pairs' groups, at most
+    # max(ceil(4096 / Hkv) + groups, groups * ceil(W / 128)) pairs (SEQ: groups = B = 4)
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    pairs = max(4096 // 8 + 4, 4 * 1)
+    assert need1 == a256(4 * 32 * 2 * 4) + a256((4 + 3) * 4) + a256(pairs * 4)
     need4 = L.pa_decode_scored_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
     assert need4 == need1 + L.pa_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(s), 32, 4)
     assert sc(ws=None) == -3                                  # always needs a workspace
