@@ -86,8 +86,14 @@ def test_more_than_1024_groups():
     _balanced_case(w, seqs=[0, 1, 3, 500, 1023, 1024, 1050, 1099])
 
 
-def test_multi_query_balanced():
-    w = make_workload(2, batch=5, lens=[4, 9, 3000, 700, 8000], q_len=4, table_width=512)
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_multi_query_balanced(cfg):
+    # SEQ (pairs of 8 heads) and HEAD (one head per pair; slots by unit)
+    if cfg == 2:
+        w = make_workload(2, batch=5, lens=[4, 9, 3000, 700, 8000], q_len=4, table_width=512)
+    else:
+        lens = np.array([[4, 2000, 9, 700, 4096, 5, 64, 33], [3000, 4, 17, 8, 1000, 4095, 16, 250]])
+        w = make_workload(4, lens=lens, q_len=4, table_width=256)
     run_case(w, partitions=(0,))
 
 
