@@ -90,8 +90,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // How a call splits each unit's pages.  Fixed: chunk_pages per partition,
 // parts partitions (an explicit count, prefill, and tables of at most
-// kPlanMinChunk pages).  Planned (automatic decode): plan_kernel picks the
-// chunk on the device from the real lengths, for about kTargetWaves waves of
+// kPlanMinChunk pages).  Planned (automatic decode): plan_block picks the
+// chunk on the device from the real lengths, for at most kPlanWaves waves of
 // equal work; a plan holds at most max_pairs (group, partition) pairs.
 #ifndef PA_PLAN_WAVES
 #define PA_PLAN_WAVES 2048

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   __shared__ bf16x8 s_q[QLDS ? kWaves : 1][QLDS ? NQ * NSTEP : 1][64];
 
   const int Pn = a.num_parts;
-  const bool planned = a.plan != nullptr;      // length-balanced split (see plan_kernel)
+  const bool planned = a.plan != nullptr;      // length-balanced split (see plan_block)
   const int ppw = (NQ == 1 && !planned) ? a.parts_per_wave : 1;
   const int groups = (Pn + ppw - 1) / ppw;     // waves per unit (fixed partitions)
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;

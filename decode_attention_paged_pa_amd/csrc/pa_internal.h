@@ -36,7 +36,7 @@ struct AttnArgs {
   int xcd_order;             // workgroup order that keeps a page's heads on one XCD
   float score_scale_log2;    // softmax_scale * log2(e)
   // Length-balanced split (automatic partitions; nullptr: fixed partitions of
-  // chunk_pages).  Written by plan_kernel: plan[0] the chunk in pages,
+  // chunk_pages).  Written by plan_block: plan[0] the chunk in pages,
   // plan[1] the number of pairs, plan[2 + g] the first pair of group g
   // (groups + 1 entries); plan_group[pair] the group of each pair.  A group
   // is a sequence (SEQ: its Hkv heads share the pair) or a unit (HEAD); a
