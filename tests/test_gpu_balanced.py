@@ -144,3 +144,48 @@ def test_graph_replans_when_lengths_change():
     assert np.all(flags_of(dw) == 0)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     assert not torch.equal(out[3].view(torch.int16), first[3].view(torch.int16))
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def _rule_chunk(pages, hpg, W, target=2048, min_chunk=32):
+    """The planner's rule: the smallest chunk of at least min_chunk pages (at most
+    W) whose partitions, each group's last one rounded up, make <= target waves."""
+    lo = min(max(-(-int(pages.sum()) * hpg // target), min_chunk), W)
+    for c in range(lo, W + 1):
+        if int((-(-pages // c)).sum()) * hpg <= target:
+            return c
+    return W
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_plan_follows_the_rule(cfg):
+    """The plan the automatic decode leaves in its workspace (layout of
+    pa_decode_workspace_bytes in pa.h: partials, then chunk, pair count, first
+    pair of each group, group of each pair) is the rule's, exactly."""
+    w = make_workload(cfg, stale_frac=0.0)
+    dw = build_device_workload(w)
+    dw.step_append()
+    need = pa.workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dw.decode(check=True, num_partitions=0, workspace=ws)
+    torch.cuda.synchronize()
+    head = w.layout == "head"
+    hpg, groups = (1, w.B * w.Hkv) if head else (w.Hkv, w.B)
+    max_pairs = -(-2048 // hpg) + groups
+    slots = max_pairs * hpg * w.G
+    off = _a256(slots * w.D * 4) + _a256(slots * 2 * 4)
+    plan = ws[off:off + (groups + 3) * 4].cpu().numpy().view(np.int32)
+    goff = off + _a256((groups + 3) * 4)
+    pages = -(-np.clip(w.lens.reshape(-1).astype(np.int64), 0, w.W * w.S) // w.S)
+    chunk = _rule_chunk(pages, hpg, w.W)
+    parts = -(-pages // chunk)
+    first = np.concatenate([[0], np.cumsum(parts)])
+    log("plan: workload %d chunk %d pairs %d (%d waves)" % (cfg, chunk, first[-1], first[-1] * hpg))
+    assert plan[0] == chunk and plan[1] == first[-1]
+    assert np.array_equal(plan[2:2 + groups + 1], first)
+    grp = ws[goff:goff + int(first[-1]) * 4].cpu().numpy().view(np.int32)
+    assert np.array_equal(grp, np.repeat(np.arange(groups), parts))
+    assert first[-1] * hpg <= 2048
