@@ -119,7 +119,8 @@ CONFIG_NAMES = {1: "tiny", 2: "llama8b-bf16", 3: "llama8b-fp8-tags", 4: "headwis
 
 
 def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
-                  spare_pages=64, table_width=None, q_len=1, heads=None):
+                  spare_pages=64, table_width=None, q_len=1, heads=None, kv=None, layout=None,
+                  head_dim=None):
     """Draw workload `cfg_id` (1..5).
 
     batch / lens / table_width override the workload's own sizes for reduced
@@ -127,7 +128,10 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     (workload 3 defaults to 0.01, the others to 0); q_len > 1 makes the step
     a multi-query step of q_len query tokens (speculative verification: up to
     8 drafts; chunked prefill: a chunk of q_len prompt tokens);
-    heads = (Hq, Hkv) overrides the head counts (edge cases of the grouping).
+    heads = (Hq, Hkv) overrides the head counts (edge cases of the grouping);
+    kv ("bf16" | "fp8"), layout ("seq" | "head") and head_dim (64 | 128)
+    override the cache format, for the combinations no named workload uses.
+    The draws keep their order; their sizes follow the overridden shapes.
     """
     if int(q_len) < 1:
         raise ValueError("q_len must be at least 1")
@@ -146,6 +150,9 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     Hkv, Hq, D = spec["Hkv"], spec["Hq"], spec["D"]
     if heads is not None:
         Hq, Hkv = int(heads[0]), int(heads[1])
+    spec = dict(spec, kv=kv or spec["kv"], layout=layout or spec["layout"])
+    if head_dim is not None:
+        D = int(head_dim)
 
     # 1. lengths
     if lens is not None:

@@ -112,6 +112,16 @@ def test_scored_headwise():
     scored_case(make_workload(4, lens=lens), seqs=range(2), partitions=(0, 1, 16, 64))
 
 
+@pytest.mark.parametrize("layout,D", [("head", 128), ("head", 64), ("seq", 64)])
+def test_scored_fp8_other_formats(layout, D):
+    if layout == "head":
+        lens = np.array([[33, 1, 512, 16, 17, 100, 5, 64], [2048, 8, 4096, 4097, 15, 16, 31, 1000]])
+    else:
+        lens = [5, 700, 2049, 5000]
+    w = make_workload(2, lens=lens, kv="fp8", layout=layout, head_dim=D, stale_frac=0.0)
+    scored_case(w, seqs=range(w.B), partitions=(0, 4))
+
+
 def test_scored_workload5_full_size_sampled():
     scored_case(make_workload(5), seqs=[0, 41], partitions=(8,))
 
@@ -164,6 +174,9 @@ def _unit_arrays(w, keep, n_keep):
     (4, dict(lens=np.array([[33, 1, 512, 16, 17, 100, 5, 64], [2048, 8, 4096, 4097, 15, 16, 31, 1000]]),
              spare_pages=700), 0.125),
     (1, dict(spare_pages=64), 0.5),
+    (2, dict(lens=np.array([[33, 1, 512, 16, 17, 100, 5, 64], [300, 8, 1000, 4097, 15, 16, 31, 90]]),
+             kv="fp8", layout="head", head_dim=64, spare_pages=200), 0.25),
+    (2, dict(batch=3, lens=[40, 333, 1500], kv="fp8", head_dim=64, spare_pages=96), 0.5),
 ])
 def test_compaction_matches_oracle(cfg, kw, frac):
     w = make_workload(cfg, **kw)

@@ -55,6 +55,16 @@ def test_multi_bf16_ragged_and_partition_boundary_inside_drafts():
     run_case(w, partitions=(0, 1, 3, 8, 64))
 
 
+@pytest.mark.parametrize("layout,D,T", [("head", 128, 3), ("head", 64, 8), ("seq", 64, 5)])
+def test_multi_fp8_other_formats(layout, D, T):
+    if layout == "head":
+        lens = np.array([[8, 300, 17, 2049, 9, 100, 1000, 64], [4096, 12, 650, 33, 8, 700, 64, 90]])
+    else:
+        lens = [8, 300, 2049, 5000]
+    w = make_workload(2, lens=lens, kv="fp8", layout=layout, head_dim=D, q_len=T, stale_frac=0.0)
+    run_case(w, partitions=(0, 2))
+
+
 def test_multi_fp8_stale_tags():
     w = make_workload(3, batch=5, lens=[5, 700, 2049, 5000, 9000], q_len=5, stale_frac=0.02)
     assert w.stale.any()

@@ -145,6 +145,20 @@ def test_workload3_full_stale_then_valid():
     compare_outputs(out, ora, range(w.B), flags_of(dw), "all tags valid")
 
 
+@pytest.mark.parametrize("layout,kv,D", [("head", "fp8", 128), ("head", "fp8", 64),
+                                          ("head", "bf16", 64), ("seq", "fp8", 64)])
+def test_cache_format_combinations(layout, kv, D):
+    """Cache formats no named workload uses (the llama8b-bf16 shape with the format
+    overridden), stale tags included: every layout x dtype x head size the C ABI takes."""
+    if layout == "head":
+        lens = np.array([[1, 17, 300, 1500, 4097, 16, 33, 900],
+                         [2048, 5, 64, 65, 700, 4096, 1, 250]])
+    else:
+        lens = [1, 17, 300, 1500, 4097]
+    w = make_workload(2, lens=lens, kv=kv, layout=layout, head_dim=D, stale_frac=0.02)
+    run_case(w, partitions=(0, 1, 3))
+
+
 def test_workload4_headwise_full():
     run_case(make_workload(4), partitions=(0, 16, 64))
 

@@ -27,6 +27,9 @@ pytestmark = pytest.mark.gpu
     (3, dict(batch=2, lens=[300, 2000], stale_frac=0.02), 128, (0, 2)),   # FP8, stale tags
     (1, dict(lens=[40, 64, 300, 511], heads=(16, 1)), 40, (0, 2)),        # G 16, Hkv 1
     (2, dict(batch=2, lens=[100, 700], heads=(24, 8)), 97, (0, 3)),       # G 3: ragged blocks
+    (2, dict(lens=np.array([[80, 300, 700, 1000, 90, 2000, 65, 64], [64, 100, 4000, 70, 99, 640, 300, 1000]]),
+             kv="fp8", layout="head"), 64, (0, 2)),                       # FP8, HEAD
+    (2, dict(batch=2, lens=[200, 1500], kv="fp8", head_dim=64), 100, (0, 2)),   # FP8, D 64
 ])
 def test_prefill_matches_oracle(cfg, kw, C, parts):
     w = make_workload(cfg, q_len=C, **kw)
