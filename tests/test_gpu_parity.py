@@ -159,6 +159,21 @@ def test_cache_format_combinations(layout, kv, D):
     run_case(w, partitions=(0, 1, 3))
 
 
+@pytest.mark.parametrize("heads,layout,kv", [((8, 8), "seq", "fp8"), ((32, 32), "head", "bf16"),
+                                              ((12, 6), "seq", "bf16"), ((12, 6), "head", "fp8")])
+def test_group_sizes(heads, layout, kv):
+    """G = 1 (as many query heads as KV heads, one valid column per MFMA tile) and
+    Hkv = 6 (not a multiple of 4: the plain workgroup order), both layouts."""
+    Hkv = heads[1]
+    if layout == "head":
+        rng = np.random.default_rng(Hkv)
+        lens = rng.integers(1, 3000, size=(3, Hkv)).astype(np.int32)
+    else:
+        lens = [1, 700, 2900]
+    w = make_workload(2, lens=lens, heads=heads, kv=kv, layout=layout, stale_frac=0.02)
+    run_case(w, partitions=(0, 1, 4))
+
+
 def test_workload4_headwise_full():
     run_case(make_workload(4), partitions=(0, 16, 64))
 
