@@ -192,6 +192,24 @@ def test_workload5_full_size_sampled():
     assert np.abs(got).max() < 6.5
 
 
+@pytest.mark.timeout(900)
+def test_bf16_pools_beyond_4gib_sampled():
+    """The 70B shape with a BF16 cache: each pool is 4.3 GB, so page offsets pass
+    2^32 bytes (64-bit address arithmetic in append, validation and decode).  Two
+    sampled sequences that hold pages past the 4 GiB mark are checked against
+    the oracle; all rows are checked finite."""
+    w = make_workload(5, kv="bf16", stale_frac=0.0)
+    per_page = w.Hkv * w.S * w.D * 2
+    far = [b for b in range(w.B)
+           if (w.block_table[b][: -(-int(w.lens[b]) // w.S)].astype(np.int64) * per_page
+               >= 1 << 32).any()]
+    assert len(far) >= 2, far
+    sampled = far[:2]
+    dw, ora, outs = run_case(w, seqs=sampled, partitions=(0,), pools=False)
+    got = out_f64(outs[0])
+    assert np.all(np.isfinite(got))
+
+
 def _custom_cache_case(K, V, q, S=16, kv="bf16"):
     """One sequence (Hkv = 1) with given K/V tokens, on GPU and in the oracle."""
     L, D = K.shape
