@@ -171,30 +171,37 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     move_scores();
     return;
   } else {
-    // FP8: x = fl32(dec(c) * s_old), decoded once (four codes per two pair
-    // conversions); amax over the wave; re-encode under s_new.  The encode is
-    // gfx950's fp32 -> OCP e4m3 pair conversion: round to nearest even, sign
-    // kept on underflow, and equal to the saturating definition (e4m3_rne_sat)
-    // for every finite |v| <= 464, which holds every quotient here
-    // (|x| <= amax, s_new = fl32(amax / 448)); checked exhaustively on MI355X.
-    float x[CPL][16];
+    // FP8: x = fl32(dec(c) * s_old), decoded with gfx950's pair conversions
+    // (four codes per two instructions) once for the amax over the wave and
+    // again for the re-encode under s_new, rather than kept: 64 more live
+    // registers would cost this latency-bound kernel waves per SIMD.  The
+    // encode is the fp32 -> OCP e4m3 pair conversion: round to nearest even,
+    // sign kept on underflow, and equal to the saturating definition
+    // (e4m3_rne_sat) for every finite |v| <= 464, which holds every quotient
+    // here (|x| <= amax, s_new = fl32(amax / 448)); checked exhaustively on
+    // MI355X.
+    auto decode4 = [&](int r, int w4, float (&x)[4]) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[r][w4], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[r][w4], true);
+      const float dec[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = w4 * 4 + i;
+        x[i] = ((valid[r] >> e) & 1u) ? __fmul_rn(dec[i], esc[r][e & 3]) : 0.f;
+      }
+    };
     float mk = 0.f, mv = 0.f;
 #pragma unroll
     for (int r = 0; r < CPL; ++r) {
       const bool is_k = r * 64 + lane < NCH;
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[r][w4], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[r][w4], true);
-        const float dec[4] = {lo.x, lo.y, hi.x, hi.y};
+        float x[4];
+        decode4(r, w4, x);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = w4 * 4 + i;
-          const float v = __fmul_rn(dec[i], esc[r][e & 3]);
-          const bool ok = (valid[r] >> e) & 1u;
-          x[r][e] = ok ? v : 0.f;
-          if (is_k) mk = fmaxf(mk, fabsf(x[r][e]));
-          else mv = fmaxf(mv, fabsf(x[r][e]));
+          if (is_k) mk = fmaxf(mk, fabsf(x[i]));
+          else mv = fmaxf(mv, fabsf(x[i]));
         }
       }
     }
@@ -212,11 +219,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
       if (s_new != 0.f) {
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
+          float x[4];
+          decode4(r, w4, x);
           int word = 0;
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x[r][4 * w4 + 0], s_new),
-                                                 __fdiv_rn(x[r][4 * w4 + 1], s_new), word, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x[r][4 * w4 + 2], s_new),
-                                                 __fdiv_rn(x[r][4 * w4 + 3], s_new), word, true);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x[0], s_new), __fdiv_rn(x[1], s_new),
+                                                 word, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x[2], s_new), __fdiv_rn(x[3], s_new),
+                                                 word, true);
           enc[w4] = (uint32_t)word;
         }
       }
