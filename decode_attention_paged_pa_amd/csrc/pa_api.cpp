@@ -239,6 +239,24 @@ int check_prefill(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, int3
   return PA_OK;
 }
 
+// Arguments of one planner workgroup (see plan_block): group lengths are the
+// sequence's (SEQ) or the unit's (HEAD) entries of seq->lens.
+pa::PlanArgs plan_args(const pa_seq_desc* seq, const Split& sp, char* plan, char* group,
+                       int target_waves, int min_chunk, int max_chunk) {
+  pa::PlanArgs p{};
+  p.lens = seq->lens;
+  p.plan = reinterpret_cast<int32_t*>(plan);
+  p.plan_group = reinterpret_cast<int32_t*>(group);
+  p.num_groups = sp.groups;
+  p.heads_per_group = sp.hpg;
+  p.table_width = seq->table_width;
+  p.max_pairs = sp.max_pairs;
+  p.target_waves = target_waves;
+  p.min_chunk = min_chunk;
+  p.max_chunk = max_chunk;
+  return p;
+}
+
 int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
                 int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
                 int32_t num_partitions, uint32_t* flags, void* workspace, size_t workspace_bytes,
@@ -287,33 +305,12 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
     v.head_layout = head;
   }
   char* ws = static_cast<char*>(workspace);
-  pa::PlanArgs pl{};
-  if (sp.planned) {
-    pl.lens = seq->lens;
-    pl.plan = reinterpret_cast<int32_t*>(ws + wl.plan);
-    pl.plan_group = reinterpret_cast<int32_t*>(ws + wl.plan_group);
-    pl.num_groups = sp.groups;
-    pl.heads_per_group = sp.hpg;
-    pl.table_width = seq->table_width;
-    pl.max_pairs = sp.max_pairs;
-    pl.target_waves = (int)kPlanWaves;
-    pl.min_chunk = kPlanMinChunk;
-    pl.max_chunk = seq->table_width;
-  }
-  pa::PlanArgs pm{};
+  // the decode's split (automatic) and the score pass's split (scored decode)
   const Split ms = scores ? mass_split(cache, seq) : Split{};
-  if (scores) {
-    pm.lens = seq->lens;
-    pm.plan = reinterpret_cast<int32_t*>(ws + wl.mass_plan);
-    pm.plan_group = reinterpret_cast<int32_t*>(ws + wl.mass_group);
-    pm.num_groups = ms.groups;
-    pm.heads_per_group = ms.hpg;
-    pm.table_width = seq->table_width;
-    pm.max_pairs = ms.max_pairs;
-    pm.target_waves = kMassPlanWaves;
-    pm.min_chunk = kMassMinChunk;
-    pm.max_chunk = pa::kMassRun;
-  }
+  const pa::PlanArgs pl = plan_args(seq, sp, ws + wl.plan, ws + wl.plan_group, (int)kPlanWaves,
+                                    kPlanMinChunk, seq->table_width);
+  const pa::PlanArgs pm = plan_args(seq, ms, ws + wl.mass_plan, ws + wl.mass_group,
+                                    kMassPlanWaves, kMassMinChunk, pa::kMassRun);
   if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, scores ? &pm : nullptr,
                       stream) != hipSuccess)
     return PA_ERR_LAUNCH;
