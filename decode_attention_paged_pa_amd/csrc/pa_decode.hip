@@ -24,6 +24,8 @@ namespace {
 // sums and f16/bf16 MFMA operands hold without loss of range.
 constexpr float kRescaleSlack = 8.0f;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Tuning knobs (fixed at build time; the defaults are the measured best).
 #ifndef PA_PIPE_DEPTH
 #define PA_PIPE_DEPTH 2        // pages held in registers per wave (loads in flight + current)
@@ -48,6 +50,12 @@ constexpr float kRescaleSlack = 8.0f;
 #endif
 #ifndef PA_MQ_THROTTLE
 #define PA_MQ_THROTTLE 1
+#endif
+#ifndef PA_MQ_LATE_K
+#define PA_MQ_LATE_K 1         // 4 tiles: one K buffer, next page requested after Q.K
+#endif
+#ifndef PA_QK_SCHED
+#define PA_QK_SCHED 4          // several tiles: Q reads kept this far ahead of Q.K (0: compiler's order)
 #endif
 #ifndef PA_MQ_WAVES2
 #define PA_MQ_WAVES2 0         // occupancy hint with 2 column tiles (0: derived below)
@@ -312,6 +320,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   constexpr int NSTEP = D / 32;                // QK MFMA steps over d
   constexpr int PIPE = NQ == 1 ? kPipe : PA_MQ_PIPE_DEPTH;
   constexpr bool THROTTLE = NQ == 1 ? PA_THROTTLE : PA_MQ_THROTTLE;
+  // Four-tile kernels (prefill, 8 drafts) hold one K buffer instead of two:
+  // measured on MI355X, 4-5% faster there, 3% slower with two tiles.
+  constexpr bool LATEK = NQ == 4 && PA_MQ_LATE_K;
+  static_assert(!LATEK || PIPE == 2, "one K and two V buffers");
   // A wave streams at most two partitions (single-tile kernels only); the
   // state of the first is parked here (O, max, per-lane sum; one column per
   // lane) until the wave ends.
@@ -469,13 +481,21 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // first token that some column cannot see: pages at or past it need masks
   const int vis_min = CAUSAL ? L - T + cbase / G + 1 : L;
 
+  // Running max before a column's first visible token.  Causal kernels start
+  // from the lowest finite float rather than -inf: a column with nothing
+  // visible yet then needs no special case (exp2(-inf - m) = 0 for its masked
+  // scores, and a rescale that finds no visible score leaves it at alpha = 1),
+  // and the first visible score replaces it with alpha = exp2(-FLT_MAX - m) = 0
+  // exactly as from -inf.  Partials of such columns are never merged (the
+  // reduce reads only partitions that hold a visible token of the row).
+  constexpr float kEmptyMax = CAUSAL ? -3.40282347e38f : -INFINITY;
   f32x4 o[NQ][NT];
   float m_run[NQ], l_acc[NQ];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) o[nq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[nq] = -INFINITY;
+    m_run[nq] = kEmptyMax;
     l_acc[nq] = 0.f;
   }
 
@@ -554,11 +574,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  auto compute = [&](const u32x4 (&kr)[NSEG], const u32x4 (&vr)[NSEG], float ksc, float vsc,
-                     int k) {
-    const int page = p0 + k;
-    float kfac = a.score_scale_log2;
-    if (FP8) kfac *= ksc;
+  // S^T of one page: acc[nq] = K Q^T for column tile nq (unscaled)
+  auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NSEG]) {
     // Q operand of tile nq, step st; the LDS index carries a per-page zero the
     // compiler cannot see through, so the reads are not hoisted out of the
     // page loop (which would put Q back into registers)
@@ -568,67 +585,116 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       if constexpr (QLDS) return s_q[wave][nq * NSTEP + st][lane + qz];
       else return qop[nq][st];
     };
-    // ---- scores S^T (token rows x query columns), one accumulator per tile
-    f32x4 acc[NQ];
+    // K operand of step st (16 tokens x 32 dims): FP8 codes widened to bf16
+    auto kv = [&](int st) -> bf16x8 {
+      if constexpr (FP8) {
+        const int i = st >> 1, hh = st & 1;
+        u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
+        u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      } else {
+        return __builtin_bit_cast(bf16x8, kr[st]);
+      }
+    };
+    // ---- scores S^T (token rows x query columns), one accumulator per tile;
+    // the Q operands of step st + 1 are requested before step st's MFMAs
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) acc[nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qn[NQ];
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i) {
-      if (FP8) {
+    for (int nq = 0; nq < NQ; ++nq) qn[nq] = qv(nq, 0);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
-          u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    for (int st = 0; st < NSTEP; ++st) {
+      bf16x8 qc[NQ];
 #pragma unroll
-          for (int nq = 0; nq < NQ; ++nq)
-            acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qv(nq, 2 * i + hh), acc[nq],
-                                                              0, 0, 0);
-        }
-      } else {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, kr[i]);
+      for (int nq = 0; nq < NQ; ++nq) qc[nq] = qn[nq];
+      if (st + 1 < NSTEP) {
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq)
-          acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qv(nq, i), acc[nq], 0, 0, 0);
+        for (int nq = 0; nq < NQ; ++nq) qn[nq] = qv(nq, st + 1);
       }
+      const bf16x8 av = kv(st);
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq)
+        acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qc[nq], acc[nq], 0, 0, 0);
     }
-    // lane (c, q4) now holds the scores of column c of each tile for tokens 4*q4 + r
+#if PA_QK_SCHED
+    if constexpr (QLDS) {
+      // Keep PA_QK_SCHED LDS reads of Q ahead of the MFMAs that use them.  Left
+      // to itself the compiler waited for each read just before its MFMA,
+      // exposing the LDS latency 12 times per page (measured on MI355X: 17-19%
+      // of the prefill kernel's time); 5 or more ahead spill with BF16 pages.
+      constexpr int nr = NQ * NSTEP, ahead = PA_QK_SCHED;
+      __builtin_amdgcn_sched_group_barrier(0x100, ahead, 0);
+#pragma unroll
+      for (int i = 0; i < nr - ahead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
+    }
+#endif
+  };
+
+  // Softmax update and O^T += V^T P^T for page k of the run, from its scores.
+  auto pv = [&](const f32x4 (&acc)[NQ], const u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
+    const int page = p0 + k;
+    float kfac = a.score_scale_log2;
+    if (FP8) kfac *= ksc;
+    // lane (c, q4) holds the scores of column c of each tile for tokens 4*q4 + r
     const int tok0 = page * kPageSize + q4 * 4;
     const bool tail = page * kPageSize + kPageSize > vis_min;
     f16x4 pbh[NQ];   // FP8: P^T operands (f16); BF16 uses pbb
     i16x4 pbb[NQ];
+    // The running max of a column moves only when one of its scores exceeds
+    // it by more than the slack.  A lane's own max over its 4 tokens decides
+    // that as well as the column max does (the ballot is over the whole wave
+    // and the column's 4 lanes share m_run), so the cross-lane column max is
+    // only formed on the rare pages that rescale.
+    float sc[NQ][4], lmax[NQ];
+    bool grow = false;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[nq][r] = acc[nq][r] * kfac;
+    if (tail) {
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[nq][r] = (tok0 + r < lim[nq]) ? sc[nq][r] : -INFINITY;
+    }
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
-      float sc[4];
+      lmax[nq] = fmaxf(fmaxf(sc[nq][0], sc[nq][1]), fmaxf(sc[nq][2], sc[nq][3]));
+      grow |= lmax[nq] > m_run[nq] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = acc[nq][r] * kfac;
-      if (tail) {
+      for (int nq = 0; nq < NQ; ++nq) {
+        if (__builtin_amdgcn_ballot_w64(lmax[nq] > m_run[nq] + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run[nq], col_max(lmax[nq]));
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nq] - m_new);
+          l_acc[nq] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim[nq]) ? sc[r] : -INFINITY;
+          for (int j = 0; j < NT; ++j) o[nq][j] *= alpha;
+          m_run[nq] = m_new;
+        }
       }
-      float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mloc = col_max(mloc);
-      if (__builtin_amdgcn_ballot_w64(mloc > m_run[nq] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[nq], mloc);
-        // a column that has seen no token yet keeps -inf on both sides
-        const float alpha = (CAUSAL && m_new == -INFINITY) ? 1.f
-                                                           : __builtin_amdgcn_exp2f(m_run[nq] - m_new);
-        l_acc[nq] *= alpha;
+    }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) o[nq][j] *= alpha;
-        m_run[nq] = m_new;
-      }
-      const float mref = (CAUSAL && m_run[nq] == -INFINITY) ? 0.f : m_run[nq];
+    for (int nq = 0; nq < NQ; ++nq) {
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - mref);
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[nq][r] - m_run[nq]);
       l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
       if (FP8) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) pbh[nq][r] = (_Float16)(p[r] * vsc);
       } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pbb[nq][r] = __builtin_bit_cast(short, (__bf16)p[r]);
+        // two values per conversion (round to nearest even, as one by one)
+        const bf16x2 lo = __builtin_convertvector(f32x2{p[0], p[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector(f32x2{p[2], p[3]}, bf16x2);
+        pbb[nq] = __builtin_bit_cast(i16x4, u32x2{__builtin_bit_cast(uint32_t, lo),
+                                                 __builtin_bit_cast(uint32_t, hi)});
       }
     }
 
@@ -667,6 +733,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
           o[nq][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pbb[nq], o[nq][j], 0, 0, 0);
       }
     }
+  };
+
+  auto compute = [&](const u32x4 (&kr)[NSEG], const u32x4 (&vr)[NSEG], float ksc, float vsc,
+                     int k) {
+    f32x4 acc[NQ];
+    qk(acc, kr);
+    pv(acc, vr, ksc, vsc, k);
   };
 
   // This wave's result for partition `part`: the normalised output when the
@@ -739,6 +812,24 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       asm volatile("" : : "s"(lastsc));
     }
     id_chunk = 0;
+    if constexpr (LATEK) {
+      // One K buffer: page r+1 is requested as soon as page r's Q.K has read
+      // K, and the waits are the compiler's (K before Q.K, V before P.V)
+      load(kr[0], vr[0], ks[0], vs[0], 0);
+      for (int r0 = 0; r0 < m; r0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = r0 + u;
+          if (r < m) {
+            f32x4 acc[NQ];
+            qk(acc, kr[0]);
+            if (r + 1 < m) load(kr[0], vr[1 - u], ks[1 - u], vs[1 - u], r + 1);
+            pv(acc, vr[u], ks[u], vs[u], seg + r);
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int u = 0; u < PIPE - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1));
     for (int r0 = 0; r0 < m; r0 += PIPE) {
