@@ -1,24 +1,30 @@
 """Benchmark of one paged-decode step on one MI355X.
 
-A step is the whole hot path for one batch: pa_cache_append of the step's new
-token for every (sequence, KV head), then pa_decode (page-tag validation,
-split-K attention, partition reduce).  Inputs are synthetic and seeded
-(decode_attention_paged_pa_amd.workloads) and resident in HBM before timing.
+A step is the whole hot path for one batch: the append of the step's new
+token for every (sequence, KV head), then the decode (page-tag validation,
+split-K attention, partition reduce), made as one pa_decode_step call: the
+append shares the validation's launch, so a step is three launches
+(--separate-append: pa_cache_append then pa_decode, four launches).  Inputs
+are synthetic and seeded (decode_attention_paged_pa_amd.workloads) and
+resident in HBM before timing.
 
 Default workload: the 70B-shaped FP8 layer, B 64, 64 query / 8 KV heads,
 D 128, 32768 tokens per sequence (4.29 GB of FP8 KV), split-K 8, tag check on.
 
 Timing: W untimed warm-up steps; then K steps, each preceded (outside the
 timed events) by a 512 MiB write that evicts L2 and the Infinity Cache; HIP
-events on the launch stream bracket the step and each kernel.  The K steps
-are also bracketed by device synchronisation for a wall-clock figure.
+events on the launch stream bracket each step.  The K steps are also
+bracketed by device synchronisation for a wall-clock figure.  A second pass
+of K steps records events between the kernels as well, for the per-kernel
+split and the attention kernel's roofline (an event between two kernels
+costs a few microseconds itself, so the timed steps carry none).
 
 Prints one JSON line.  `value` is the achieved HBM GB/s of the step
 (algorithmic bytes / mean step time); `roofline` is the attention kernel
 against the 8 TB/s HBM peak; `cpu_baseline` is the fp64 oracle's decode on a
 bounded sample of the same workload, on this host's cores.  `graph` is the
-same step captured once as a HIP graph and replayed K times (one launch per
-step instead of five).
+same step captured once as a HIP graph and replayed K times (one graph launch
+per step instead of three kernel launches).
 
 --q-len T (2..8) turns the step into a multi-query step (speculative
 verification): the append writes T draft tokens per unit and
@@ -108,7 +114,7 @@ def compaction_bytes(w, n_keep_units):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h"):
+    for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h", "pa_block.h"):
         with open(os.path.join(ROOT, "decode_attention_paged_pa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -285,6 +291,8 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="draft tokens per sequence (multi-query step), 1..8")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append and decode as two calls (four launches) instead of pa_decode_step")
     ap.add_argument("--scored", action="store_true", help="scored decode (eviction scores)")
     ap.add_argument("--compact", type=float, default=0.0,
                     help="time compaction to this fraction of the tokens instead")
@@ -352,9 +360,17 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    # a decode step is pa_decode_step (its append shares the validation's launch),
+    # or, with --separate-append, the scored decode and prefill, two calls
+    fused = not args.separate_append and not args.scored and args.prefill == 0
+
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
+        if fused:
+            dw.decode_step(check=check, num_partitions=parts, out=out, workspace=workspace,
+                           events=None if evs is None else evs[1:])
+            return
         dw.step_append()
         if args.scored:
             pa.decode_scored(dw.cache, dw.q, dw.block_table, dw.lens, w.sigma, scores,
@@ -370,8 +386,13 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Timed steps carry two events each (start, end): an event recorded
+    # between kernels costs a few microseconds of its own on this stack, so
+    # the per-kernel split comes from a second pass of K steps with events
+    # between the launches (the same work, same flushes).
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    for e in evs:
+    for e in sev + evs:
         for x in e:
             x.record(stream)   # create the underlying events before timing
     torch.cuda.synchronize()
@@ -379,10 +400,18 @@ def main():
     for k in range(K):
         if not args.no_flush:
             flush.zero_()
-        step(evs[k])
+        sev[k][0].record(stream)
+        step()
+        sev[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    t_step = np.array([e[0].elapsed_time(e[4]) for e in evs])          # ms
+    for k in range(K):
+        if not args.no_flush:
+            flush.zero_()
+        step(evs[k])
+    torch.cuda.synchronize()
+    t_step = np.array([e[0].elapsed_time(e[1]) for e in sev])          # ms
+    t_split = np.array([e[0].elapsed_time(e[4]) for e in evs])
     t_append = np.array([e[0].elapsed_time(e[1]) for e in evs])
     t_val = np.array([e[1].elapsed_time(e[2]) for e in evs])
     t_attn = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -392,9 +421,12 @@ def main():
     gbs = by["step"] / (ms * 1e-3) / 1e9
     attn_gbs = by["attention_kernel"] / (t_attn.mean() * 1e-3) / 1e9
     tok_s = w.B * T / (ms * 1e-3)
-    log("step %.3f ms (p10 %.3f p90 %.3f); append %.1f us, validate %.1f us, attention %.1f us, "
+    log("step %.3f ms (p10 %.3f p90 %.3f; %.3f ms with events between the kernels); append "
+        "%.1f us, %s %.1f us, attention %.1f us, "
         "reduce%s %.1f us; %.0f GB/s step, attention %.0f GB/s (%.1f%% of 8 TB/s)" % (
-            ms, np.percentile(t_step, 10), np.percentile(t_step, 90), t_append.mean() * 1e3,
+            ms, np.percentile(t_step, 10), np.percentile(t_step, 90), t_split.mean(),
+            t_append.mean() * 1e3,
+            "append+validate (one launch)" if fused else "validate",
             t_val.mean() * 1e3, t_attn.mean() * 1e3, " + score" if args.scored else "",
             t_red.mean() * 1e3, gbs, attn_gbs,
             100 * attn_gbs / HBM_PEAK_GBS))
@@ -488,10 +520,13 @@ def main():
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tok_s, 1),
         "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
-        "kernels_us": {"append": round(t_append.mean() * 1e3, 2),
-                       "validate": round(t_val.mean() * 1e3, 2),
+        "ms_per_step_with_kernel_events": round(float(t_split.mean()), 4),
+        "kernels_us": ({"append+validate": round(t_val.mean() * 1e3, 2)} if fused else
+                       {"append": round(t_append.mean() * 1e3, 2),
+                        "validate": round(t_val.mean() * 1e3, 2)}) | {
                        "attention": round(t_attn.mean() * 1e3, 2),
                        ("reduce+score" if args.scored else "reduce"): round(t_red.mean() * 1e3, 2)},
+        "step_calls": "pa_decode_step (3 launches)" if fused else "pa_cache_append + decode",
         "algorithmic_bytes": by,
         "graph": graph,
         "roofline": {

@@ -257,11 +257,44 @@ pa::PlanArgs plan_args(const pa_seq_desc* seq, const Split& sp, char* plan, char
   return p;
 }
 
+// Arguments of an append of n_new[u] tokens (at most n_max) at positions
+// lens_old[u]... through seq's table; k_new / v_new are [B][Hkv][n_max][D].
+int append_args(const pa_cache_desc* cache, const pa_seq_desc* seq, const int32_t* lens_old,
+                const int32_t* n_new, int32_t n_max, const uint16_t* k_new,
+                const uint16_t* v_new, pa::AppendArgs* out) {
+  if (!lens_old || !aligned(lens_old, 4) || !n_new || !aligned(n_new, 4) || n_max < 0)
+    return PA_ERR_INVALID_ARG;
+  if (n_max > 0 && (!k_new || !v_new || !aligned(k_new, 2) || !aligned(v_new, 2)))
+    return PA_ERR_INVALID_ARG;
+  pa::AppendArgs a{};
+  a.k_pages = static_cast<uint8_t*>(cache->k_pages);
+  a.v_pages = static_cast<uint8_t*>(cache->v_pages);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = seq->block_table;
+  a.lens_old = lens_old;
+  a.n_new = n_new;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.batch = seq->batch;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.table_width = seq->table_width;
+  a.num_pages = cache->num_pages;
+  a.n_max = n_max;
+  a.pages_per_unit = n_max == 0 ? 0 : (n_max + pa::kPageSize - 1) / pa::kPageSize + 1;
+  a.head_layout = cache->layout == PA_LAYOUT_HEAD;
+  a.fp8 = cache->kv_dtype == PA_KV_FP8_E4M3;
+  if ((int64_t)a.batch * a.num_kv_heads * a.pages_per_unit > INT32_MAX) return PA_ERR_INVALID_ARG;
+  *out = a;
+  return PA_OK;
+}
+
 int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_q_heads,
                 int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
                 int32_t num_partitions, uint32_t* flags, void* workspace, size_t workspace_bytes,
                 hipStream_t stream, pa_event_t const* events, float* scores = nullptr,
-                bool prefill = false) {
+                bool prefill = false, const pa::AppendArgs* app = nullptr) {
   int rc;
   if ((rc = check_cache(cache)) != PA_OK) return rc;
   if ((rc = check_seq(seq)) != PA_OK) return rc;
@@ -312,7 +345,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   const pa::PlanArgs pm = plan_args(seq, ms, ws + wl.mass_plan, ws + wl.mass_group,
                                     kMassPlanWaves, kMassMinChunk, pa::kMassRun);
   if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, scores ? &pm : nullptr,
-                      stream) != hipSuccess)
+                      app, stream) != hipSuccess)
     return PA_ERR_LAUNCH;
   rec(1);
 
@@ -390,35 +423,12 @@ PA_API int pa_cache_append(const pa_cache_desc* cache, const pa_seq_desc* seq,
   int rc;
   if ((rc = check_cache(cache)) != PA_OK) return rc;
   if ((rc = check_seq(seq)) != PA_OK) return rc;
-  if (!n_new || !aligned(n_new, 4) || n_max < 0) return PA_ERR_INVALID_ARG;
-  if (n_max == 0) {
-    if (!flags) return PA_OK;
-  } else if (!k_new || !v_new || !aligned(k_new, 2) || !aligned(v_new, 2)) {
-    return PA_ERR_INVALID_ARG;
-  }
-  if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
+  if (n_max == 0 && !flags && n_new && aligned(n_new, 4)) return PA_OK;
   pa::AppendArgs a{};
-  a.k_pages = static_cast<uint8_t*>(cache->k_pages);
-  a.v_pages = static_cast<uint8_t*>(cache->v_pages);
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
-  a.block_table = seq->block_table;
-  a.lens_old = seq->lens;
-  a.n_new = n_new;
-  a.k_new = k_new;
-  a.v_new = v_new;
+  if ((rc = append_args(cache, seq, seq->lens, n_new, n_max, k_new, v_new, &a)) != PA_OK)
+    return rc;
+  if (flags && !aligned(flags, 4)) return PA_ERR_INVALID_ARG;
   a.flags = flags;
-  a.batch = seq->batch;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.head_dim = cache->head_dim;
-  a.table_width = seq->table_width;
-  a.num_pages = cache->num_pages;
-  a.n_max = n_max;
-  a.pages_per_unit = n_max == 0 ? 0 : (n_max + pa::kPageSize - 1) / pa::kPageSize + 1;
-  a.head_layout = cache->layout == PA_LAYOUT_HEAD;
-  a.fp8 = cache->kv_dtype == PA_KV_FP8_E4M3;
-  const int64_t grid = (int64_t)a.batch * a.num_kv_heads * a.pages_per_unit;
-  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
   if (pa::launch_append(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
@@ -596,6 +606,47 @@ PA_API int pa_decode_multi_timed(const pa_cache_desc* cache, const pa_seq_desc* 
                                  pa_stream_t stream, pa_event_t const events[4]) {
   return decode_impl(cache, seq, num_q_heads, q_len, q, out, softmax_scale, num_partitions, flags,
                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events);
+}
+
+namespace {
+int step_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, const int32_t* lens_old,
+              const int32_t* n_new, int32_t n_max, const uint16_t* k_new, const uint16_t* v_new,
+              int32_t num_q_heads, int32_t q_len, const uint16_t* q, uint16_t* out,
+              float softmax_scale, int32_t num_partitions, uint32_t* flags, void* workspace,
+              size_t workspace_bytes, pa_stream_t stream, pa_event_t const* events) {
+  int rc;
+  if ((rc = check_cache(cache)) != PA_OK) return rc;
+  if ((rc = check_seq(seq)) != PA_OK) return rc;
+  pa::AppendArgs app{};
+  if ((rc = append_args(cache, seq, lens_old, n_new, n_max, k_new, v_new, &app)) != PA_OK)
+    return rc;
+  return decode_impl(cache, seq, num_q_heads, q_len, q, out, softmax_scale, num_partitions, flags,
+                     workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), events,
+                     nullptr, false, n_max > 0 ? &app : nullptr);
+}
+}  // namespace
+
+PA_API int pa_decode_step(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                          const int32_t* lens_old, const int32_t* n_new, int32_t n_max,
+                          const uint16_t* k_new, const uint16_t* v_new, int32_t num_q_heads,
+                          int32_t q_len, const uint16_t* q, uint16_t* out, float softmax_scale,
+                          int32_t num_partitions, uint32_t* flags, void* workspace,
+                          size_t workspace_bytes, pa_stream_t stream) {
+  return step_impl(cache, seq, lens_old, n_new, n_max, k_new, v_new, num_q_heads, q_len, q, out,
+                   softmax_scale, num_partitions, flags, workspace, workspace_bytes, stream,
+                   nullptr);
+}
+
+PA_API int pa_decode_step_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                                const int32_t* lens_old, const int32_t* n_new, int32_t n_max,
+                                const uint16_t* k_new, const uint16_t* v_new,
+                                int32_t num_q_heads, int32_t q_len, const uint16_t* q,
+                                uint16_t* out, float softmax_scale, int32_t num_partitions,
+                                uint32_t* flags, void* workspace, size_t workspace_bytes,
+                                pa_stream_t stream, pa_event_t const events[4]) {
+  return step_impl(cache, seq, lens_old, n_new, n_max, k_new, v_new, num_q_heads, q_len, q, out,
+                   softmax_scale, num_partitions, flags, workspace, workspace_bytes, stream,
+                   events);
 }
 
 PA_API const char* pa_strerror(int code) {

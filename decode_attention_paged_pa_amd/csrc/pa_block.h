@@ -1,16 +1,16 @@
 // Device helpers shared by the kernels that write cache blocks (append and
-// compaction): element offsets inside a (page, head) block, and the exact
-// fp32 -> OCP e4m3 rounding.  The layout is the one pa.h documents.
+// compaction): element offsets inside a (page, head) block, the exact
+// fp32 -> OCP e4m3 rounding, and the work of one append item.  The layout is
+// the one pa.h documents.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
-
-#pragma clang fp contract(off)
 
 // Element offset of K(t, d) inside a (page, head) block: 64-byte column
 // segments of 4*CE elements, CE = elements per 16-byte chunk.
@@ -51,5 +51,119 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
 }
 
 __device__ __forceinline__ float bf16_value(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+
+// One append item: unit item / pages_per_unit and the j-th page counted from
+// the page holding the unit's first new token (the new tokens of several
+// pages of one unit are separate items).  NTH threads (whole waves; tid in
+// [0, NTH)) share the item, and s_red / s_old are theirs alone.  FP8 pages
+// keep scale = amax / 448 over everything written since the page started
+// (rules of the KV cache quantization paragraph, "How we built the most
+// efficient inference engine for Cloudflare's network"): the new tokens'
+// amax may raise it, and then the page's earlier codes are re-quantised.
+//
+// Every thread passes the FP8 path's one barrier exactly once, whether or not
+// its item writes anything (inactive items, items past the unit's last page,
+// unwritable pages), so items of different units may share a workgroup.
+template <int D, bool FP8, int NTH>
+__device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
+                            float (&s_red)[2][NTH / 64], float (&s_old)[2]) {
+#pragma clang fp contract(off)
+  constexpr int E = FP8 ? 1 : 2;
+  constexpr int NW = NTH / 64;
+  constexpr int BLOCK_ELEMS = kPageSize * D;
+  const int Hkv = a.num_kv_heads;
+  const int unit = active ? item / a.pages_per_unit : 0;
+  const int j = item - unit * a.pages_per_unit;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const int row = a.head_layout ? unit : b;
+  int cnt = 0, slot0 = 0, t0 = 0, pid = 0;   // cnt = 0: nothing to write
+  if (active) {
+    const int lo = a.lens_old[row];
+    const int n = min(a.n_new[row], a.n_max);  // never read past the n_max inputs
+    if (lo >= 0 && n > 0) {
+      const int cap = a.table_width * kPageSize;
+      const int i = lo / kPageSize + j;
+      const int pos_lo = max(lo, i * kPageSize);
+      const int pos_hi = min(min(lo + n, (i + 1) * kPageSize), cap);
+      if (pos_lo < pos_hi) {
+        const int p = a.block_table[(size_t)row * a.table_width + i];
+        if ((unsigned)p < (unsigned)a.num_pages) {
+          pid = p;
+          slot0 = pos_lo - i * kPageSize;
+          cnt = pos_hi - pos_lo;
+          t0 = pos_lo - lo;   // index of the first token in k_new / v_new
+        }
+      }
+    }
+  }
+  const size_t blk = a.head_layout ? (size_t)pid : (size_t)pid * Hkv + h;
+  const size_t src0 = (((size_t)b * Hkv + h) * a.n_max + t0) * D;
+  const uint16_t* ks = a.k_new + src0;
+  const uint16_t* vs = a.v_new + src0;
+
+  if constexpr (!FP8) {
+    if (cnt == 0) return;
+    uint16_t* kb = reinterpret_cast<uint16_t*>(a.k_pages) + blk * BLOCK_ELEMS;
+    uint16_t* vb = reinterpret_cast<uint16_t*>(a.v_pages) +
+                   v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
+    for (int e = tid; e < cnt * D; e += NTH) {
+      const int s = e / D, d = e - s * D;
+      kb[k_elem<D, E>(slot0 + s, d)] = ks[e];
+      vb[v_elem<D, E>(slot0 + s, d)] = vs[e];
+    }
+    return;
+  } else {
+    uint8_t* kb = a.k_pages + blk * BLOCK_ELEMS;
+    uint8_t* vb =
+        a.v_pages + v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
+    // amax of the new values, K and V separately
+    float mk = 0.f, mv = 0.f;
+    for (int e = tid; e < cnt * D; e += NTH) {
+      mk = fmaxf(mk, fabsf(bf16_value(ks[e])));
+      mv = fmaxf(mv, fabsf(bf16_value(vs[e])));
+    }
+    if (tid == 0 && cnt > 0) {
+      s_old[0] = slot0 == 0 ? 0.f : a.k_scale[blk];  // a write at slot 0 starts the page afresh
+      s_old[1] = slot0 == 0 ? 0.f : a.v_scale[blk];
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+      mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+    }
+    if ((tid & 63) == 0) {
+      s_red[0][tid >> 6] = mk;
+      s_red[1][tid >> 6] = mv;
+    }
+    __syncthreads();
+    if (cnt == 0) return;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mk = fmaxf(mk, s_red[0][w]);
+      mv = fmaxf(mv, s_red[1][w]);
+    }
+    for (int which = 0; which < 2; ++which) {
+      uint8_t* pb = which ? vb : kb;
+      const uint16_t* src = which ? vs : ks;
+      const float so = s_old[which];
+      const float amax = which ? mv : mk;
+      const float cand = __fdiv_rn(amax, 448.0f);
+      const float sn = so > cand ? so : cand;  // max(s_old, fl32(amax / 448))
+      if (sn > so && slot0 > 0) {
+        for (int e = tid; e < slot0 * D; e += NTH) {
+          const int t = e / D, d = e - t * D;
+          const int off = which ? v_elem<D, E>(t, d) : k_elem<D, E>(t, d);
+          const float back = __fmul_rn(e4m3_to_f32(pb[off]), so);
+          pb[off] = (uint8_t)e4m3_rne_sat(__fdiv_rn(back, sn));
+        }
+      }
+      for (int e = tid; e < cnt * D; e += NTH) {
+        const int s = e / D, d = e - s * D;
+        const int off = which ? v_elem<D, E>(slot0 + s, d) : k_elem<D, E>(slot0 + s, d);
+        pb[off] = sn == 0.f ? (uint8_t)0 : (uint8_t)e4m3_rne_sat(__fdiv_rn(bf16_value(src[e]), sn));
+      }
+      if (tid == 0) (which ? a.v_scale : a.k_scale)[blk] = sn;
+    }
+  }
+}
 
 }  // namespace pa

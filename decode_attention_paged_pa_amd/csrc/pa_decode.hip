@@ -13,6 +13,7 @@
 // already the B operand of the second, and each lane owns the softmax state
 // of exactly one query column, so no data crosses lanes except two swaps per
 // page for the column maximum.
+#include "pa_block.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -292,6 +293,28 @@ __global__ __launch_bounds__(1024) void prep_kernel(ValidateArgs v, PlanArgs p0,
   const int x = blockIdx.x;
   if (x < nval) validate_block(v, x);
   else plan_block(x == nval ? p0 : p1);
+}
+
+// A decode step's append in the same launch as its validation and plan: the
+// append writes only pages and scales, which neither of them reads, and the
+// attention launch that follows sees all three.  Workgroups past the
+// validation and plan ones carry four append items each, one per 256 threads.
+template <int D, bool FP8>
+__global__ __launch_bounds__(1024) void step_prep_kernel(AppendArgs ap, int items,
+                                                         ValidateArgs v, PlanArgs p0,
+                                                         PlanArgs p1, int nval, int nplan) {
+  __shared__ float s_red[4][2][4];
+  __shared__ float s_old[4][2];
+  const int x = blockIdx.x;
+  if (x < nval) {
+    validate_block(v, x);
+  } else if (x < nval + nplan) {
+    plan_block(x == nval ? p0 : p1);
+  } else {
+    const int qt = threadIdx.x >> 8;
+    const int item = (x - nval - nplan) * 4 + qt;
+    append_item<D, FP8, 256>(ap, item, item < items, threadIdx.x & 255, s_red[qt], s_old[qt]);
+  }
 }
 
 // ------------------------------------------------------------- attention
@@ -1229,13 +1252,36 @@ hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p0, const PlanArgs* p1,
-                       hipStream_t s) {
-  if (!p0 && p1) return launch_prep(v, p1, nullptr, s);
+                       const AppendArgs* app, hipStream_t s) {
+  if (!p0 && p1) return launch_prep(v, p1, nullptr, app, s);
   const int nval = v ? v->batch : 0;
-  const unsigned grid = (unsigned)nval + (p0 ? 1u : 0u) + (p1 ? 1u : 0u);
+  const int nplan = (p0 ? 1 : 0) + (p1 ? 1 : 0);
+  const int64_t items = app ? (int64_t)app->batch * app->num_kv_heads * app->pages_per_unit : 0;
+  const ValidateArgs va = v ? *v : ValidateArgs{};
+  const PlanArgs pa0 = p0 ? *p0 : PlanArgs{}, pa1 = p1 ? *p1 : PlanArgs{};
+  if (items > 0) {
+    const unsigned grid = (unsigned)(nval + nplan + (items + 3) / 4);
+    const int it = (int)items;
+    if (app->head_dim == 128) {
+      if (app->fp8)
+        hipLaunchKernelGGL((step_prep_kernel<128, true>), dim3(grid), dim3(1024), 0, s, *app, it,
+                           va, pa0, pa1, nval, nplan);
+      else
+        hipLaunchKernelGGL((step_prep_kernel<128, false>), dim3(grid), dim3(1024), 0, s, *app, it,
+                           va, pa0, pa1, nval, nplan);
+    } else {
+      if (app->fp8)
+        hipLaunchKernelGGL((step_prep_kernel<64, true>), dim3(grid), dim3(1024), 0, s, *app, it,
+                           va, pa0, pa1, nval, nplan);
+      else
+        hipLaunchKernelGGL((step_prep_kernel<64, false>), dim3(grid), dim3(1024), 0, s, *app, it,
+                           va, pa0, pa1, nval, nplan);
+    }
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)(nval + nplan);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(1024), 0, s, v ? *v : ValidateArgs{},
-                     p0 ? *p0 : PlanArgs{}, p1 ? *p1 : PlanArgs{}, nval);
+  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(1024), 0, s, va, pa0, pa1, nval);
   return hipGetLastError();
 }
 

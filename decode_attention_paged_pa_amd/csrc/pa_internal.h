@@ -122,8 +122,10 @@ __host__ __device__ inline size_t v_block_slot(int pid, int h, int num_kv_heads,
 
 // Validation of v->batch sequences (v may be null) and up to two split plans
 // (p0, p1 may be null), in one launch.
+// Validation and split plans (either may be absent) in one launch; with `app`,
+// a decode step's append runs in the same launch (step_prep_kernel).
 hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p0, const PlanArgs* p1,
-                       hipStream_t s);
+                       const AppendArgs* app, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool fp8, bool head_layout,
                             hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, bool head_layout, hipStream_t s);

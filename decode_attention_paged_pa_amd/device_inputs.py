@@ -34,6 +34,15 @@ class DeviceWorkload:
         pa.append(self.cache, self.block_table, self.lens_old, self.n_step, self.k_step,
                   self.v_step, flags=flags)
 
+    def decode_step(self, check=True, num_partitions=0, out=None, workspace=None, events=None):
+        """The step's append and decode (T <= 8) in one library call."""
+        return pa.decode_step(self.cache, self.q, self.block_table, self.lens_old, self.n_step,
+                              self.k_step, self.v_step, self.lens, self.w.sigma,
+                              expected_tags=self.expected_tags if check else None,
+                              flags=self.flags if check else None,
+                              num_partitions=num_partitions, out=out, workspace=workspace,
+                              events=events)
+
     def decode(self, check=True, num_partitions=0, out=None, workspace=None, events=None):
         run = pa.decode if self.w.q_len == 1 else (pa.decode_multi if self.w.q_len <= 8
                                                    else pa.prefill)

@@ -7,12 +7,13 @@ no CPU fallback: without the built library every call raises.
 
 Entry points mirror include/pa.h: append (pa_cache_append); decode
 (pa_decode / pa_decode_timed), workspace_bytes, num_partitions; decode_multi
-(pa_decode_multi: causal drafts), multi_workspace_bytes; decode_scored
+(pa_decode_multi: causal drafts), multi_workspace_bytes; decode_step
+(pa_decode_step: append + decode in one call); decode_scored
 (pa_decode_scored: eviction scores), scored_workspace_bytes; compact
 (pa_cache_compact); prefill (pa_prefill), prefill_workspace_bytes,
 prefill_num_partitions; version.  PagedKVCache owns the pools, scales and tags
-(sized by pa_pool_bytes); DecodeStepGraph captures append + decode as one HIP
-graph.
+(sized by pa_pool_bytes); DecodeStepGraph captures a step (decode_step, or
+append + prefill) as one HIP graph.
 """
 import ctypes
 import os
@@ -99,6 +100,13 @@ def lib():
         L.pa_decode_scored_workspace_bytes.restype = sz
         L.pa_cache_compact.argtypes = [P(CacheDesc), P(SeqDesc), vp, i32, vp, vp, vp, vp, vp]
         L.pa_cache_compact.restype = ctypes.c_int
+        L.pa_decode_step.argtypes = [P(CacheDesc), P(SeqDesc), vp, vp, i32, vp, vp, i32, i32, vp,
+                                     vp, ctypes.c_float, i32, vp, vp, sz, vp]
+        L.pa_decode_step.restype = ctypes.c_int
+        L.pa_decode_step_timed.argtypes = [P(CacheDesc), P(SeqDesc), vp, vp, i32, vp, vp, i32,
+                                           i32, vp, vp, ctypes.c_float, i32, vp, vp, sz, vp,
+                                           P(vp)]
+        L.pa_decode_step_timed.restype = ctypes.c_int
         L.pa_prefill.argtypes = [P(CacheDesc), P(SeqDesc), i32, i32, vp, vp, ctypes.c_float, i32,
                                  vp, vp, sz, vp]
         L.pa_prefill.restype = ctypes.c_int
@@ -270,6 +278,63 @@ def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags
         raise ValueError("q must be [B][Hq][D]")
     return _decode(cache, q, 1, block_table, lens, softmax_scale, expected_tags, flags,
                    num_partitions, out, workspace, events, stream)
+
+
+def decode_step(cache, q, block_table, lens_old, n_new, k_new, v_new, lens, softmax_scale,
+                expected_tags=None, flags=None, num_partitions=0, out=None, workspace=None,
+                events=None, stream=None):
+    """pa_decode_step: append k_new/v_new [B][Hkv][n_max][D] (n_new[u] tokens at
+    lens_old[u]), then decode q [B][Hq][D] (or multi-query [B][T][Hq][D]) over
+    lens; the same result as append() then decode() / decode_multi()."""
+    multi = q.dim() == 4
+    if q.dim() not in (3, 4):
+        raise ValueError("q must be [B][Hq][D] or [B][T][Hq][D]")
+    q_len = q.shape[1] if multi else 1
+    sd = _seq(cache, block_table, lens, expected_tags)
+    for t, name in ((lens_old, "lens_old"), (n_new, "n_new")):
+        _need(t, name, I32)
+        if tuple(t.shape) != tuple(lens.shape):
+            raise ValueError("%s must have the shape of lens" % name)
+    _need(k_new, "k_new", BF16)
+    _need(v_new, "v_new", BF16)
+    B = block_table.shape[0]
+    if (k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B
+            or k_new.shape[1] != cache.num_kv_heads or k_new.shape[3] != cache.head_dim):
+        raise ValueError("k_new/v_new must be [B][Hkv][n_max][D]")
+    _need(q, "q", BF16)
+    if q.shape[0] != B or q.shape[-1] != cache.head_dim:
+        raise ValueError("q must be [B](...)[Hq][D] with the table's B and the cache's D")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", BF16)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if flags is not None:
+        _need(flags, "flags", U32)
+        if flags.numel() != B:
+            raise ValueError("flags must hold B words")
+    Hq = q.shape[-2]
+    need = (multi_workspace_bytes(cache, block_table, lens, Hq, q_len, num_partitions) if multi
+            else workspace_bytes(cache, block_table, lens, Hq, num_partitions))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    cd = cache.desc()
+    args = (ctypes.byref(cd), ctypes.byref(sd), _ptr(lens_old), _ptr(n_new), k_new.shape[2],
+            _ptr(k_new), _ptr(v_new), Hq, q_len, _ptr(q), _ptr(out), float(softmax_scale),
+            num_partitions, _ptr(flags), ws_ptr, ws_bytes, _stream(stream))
+    if events is None:
+        rc = lib().pa_decode_step(*args)
+    else:
+        for e in events:
+            if e is not None and not e.cuda_event:
+                e.record()
+        ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        rc = lib().pa_decode_step_timed(*args, ev)
+    if rc != 0:
+        raise PAError(rc, "pa_decode_step")
+    return out
 
 
 def decode_scored(cache, q, block_table, lens, softmax_scale, scores, expected_tags=None,
@@ -492,10 +557,14 @@ class DecodeStepGraph:
 
     def _step(self):
         (cache, bt, lens_old, n_new, k_new, v_new, q, lens, scale, exp, flags, parts) = self.args
+        if q.dim() == 3 or q.shape[1] <= 8:     # decode / multi-query: one call, three launches
+            decode_step(cache, q, bt, lens_old, n_new, k_new, v_new, lens, scale,
+                        expected_tags=exp, flags=flags, num_partitions=parts, out=self.out,
+                        workspace=self.workspace)
+            return
         append(cache, bt, lens_old, n_new, k_new, v_new)
-        run = decode if q.dim() == 3 else (decode_multi if q.shape[1] <= 8 else prefill)
-        run(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
-            out=self.out, workspace=self.workspace)
+        prefill(cache, q, bt, lens, scale, expected_tags=exp, flags=flags, num_partitions=parts,
+                out=self.out, workspace=self.workspace)
 
     def replay(self):
         self.graph.replay()

@@ -260,6 +260,41 @@ int pa_decode_multi_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
                           pa_event_t const events[4]);
 
 /*
+ * One decode step in one call: pa_cache_append of the step's new tokens,
+ * then pa_decode (q_len = 1) or pa_decode_multi (q_len 2 .. 8) over them.
+ * A decode step appends the token it produces before attending to it
+ * (the caching of attention keys and values that the paging pages describe:
+ * "How we built the most efficient inference engine for Cloudflare's
+ * network", section "Batching to feed the Tensor Cores").
+ *   seq:         the decode's view: seq->lens are the lengths after the
+ *                append, and the appended tokens go through seq->block_table.
+ *   lens_old:    device int32, seq->lens' shape: positions of the first new
+ *                token; normally lens_old[u] + n_new[u] == seq->lens[u]
+ *                (not checked).
+ *   n_new, n_max, k_new, v_new: as pa_cache_append.
+ *   everything else: as pa_decode / pa_decode_multi, including the workspace
+ *   (their *_workspace_bytes) and the flags, which are the decode's
+ *   validation of seq (the append itself sets no flag bits).
+ * Pages, scales and outputs are bit-identical to the two calls made one after
+ * the other.  The append shares the validation's launch (three launches
+ * instead of four); errors as the two calls, checked before any launch.
+ */
+int pa_decode_step(const pa_cache_desc *cache, const pa_seq_desc *seq, const int32_t *lens_old,
+                   const int32_t *n_new, int32_t n_max, const uint16_t *k_new,
+                   const uint16_t *v_new, int32_t num_q_heads, int32_t q_len, const uint16_t *q,
+                   uint16_t *out, float softmax_scale, int32_t num_partitions, uint32_t *flags,
+                   void *workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/* pa_decode_step with the timing events of pa_decode_timed (events[0] is
+ * recorded before the launch that appends and validates). */
+int pa_decode_step_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
+                         const int32_t *lens_old, const int32_t *n_new, int32_t n_max,
+                         const uint16_t *k_new, const uint16_t *v_new, int32_t num_q_heads,
+                         int32_t q_len, const uint16_t *q, uint16_t *out, float softmax_scale,
+                         int32_t num_partitions, uint32_t *flags, void *workspace,
+                         size_t workspace_bytes, pa_stream_t stream, pa_event_t const events[4]);
+
+/*
  * Chunked prefill over the paged cache ([paging]: prefill processes the
  * prompt tokens in parallel; the batcher mixes decode with chunks of prefill
  * tokens -- "How we built the most efficient inference engine for

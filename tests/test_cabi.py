@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes", "pa_strerror",
               "pa_decode_multi", "pa_decode_multi_workspace_bytes", "pa_decode_scored",
-              "pa_cache_compact", "pa_prefill", "pa_prefill_workspace_bytes"):
+              "pa_cache_compact", "pa_prefill", "pa_prefill_workspace_bytes", "pa_decode_step"):
         assert n in names
 
 
@@ -259,6 +259,31 @@ def test_append_rejects_bad_arguments():
     assert ap(_cache(head_dim=80), s) == -2
     assert ap(c, _seq(block_table=None)) == -1
     assert ap(c, s, n_max=0) == 0        # nothing to do, nothing launched
+
+
+def test_decode_step_rejects_bad_arguments():
+    L = pa.lib()
+    c, s = _cache(), _seq()
+    vp = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
+
+    def st(cc=c, ss=s, lens_old=FAKE + 8192, n_new=FAKE + 12288, n_max=1, k=FAKE, v=FAKE,
+           hq=32, q_len=1, q=FAKE, out=FAKE, scale=0.088, parts=0, flags=None):
+        return L.pa_decode_step(ctypes.byref(cc), ctypes.byref(ss), vp(lens_old), vp(n_new),
+                                n_max, vp(k), vp(v), hq, q_len, vp(q), vp(out), scale, parts,
+                                vp(flags), None, 0, None)
+    assert st(lens_old=0) == -1
+    assert st(lens_old=FAKE + 2) == -1                      # misaligned lengths
+    assert st(n_new=0) == -1
+    assert st(n_max=-1) == -1
+    assert st(k=0) == -1                                   # tokens to append need k_new
+    assert st(v=FAKE + 1) == -1
+    assert st(hq=30) == -1                                 # then the decode's own checks
+    assert st(q_len=9) == -2
+    assert st(scale=float("nan")) == -1
+    assert st(parts=4) == -3                               # its workspace, as pa_decode's
+    assert st(cc=_cache(head_dim=80)) == -2
+    assert st(ss=_seq(block_table=None)) == -1
+    assert st(ss=_seq(expected_tags=FAKE)) == -1          # a tag check needs flags
 
 
 def test_strerror_and_version():
