@@ -57,7 +57,13 @@ template <int N> struct IntC { static constexpr int value = N; };   // a compile
 #define PA_MQ_LATE_K 1         // 4 tiles: one K buffer, next page requested after Q.K
 #endif
 #ifndef PA_QK_SCHED
-#define PA_QK_SCHED 4          // several tiles: Q reads kept this far ahead of Q.K (0: compiler's order)
+#define PA_QK_SCHED 4          // two tiles: Q reads kept this far ahead of Q.K (0: compiler's order)
+#endif
+#ifndef PA_QK_SCHED4
+#define PA_QK_SCHED4 8         // four tiles: the same
+#endif
+#ifndef PA_IDREGS4
+#define PA_IDREGS4 2           // four tiles, BF16: page-id registers (64 pages each)
 #endif
 #ifndef PA_RED_THREADS
 #define PA_RED_THREADS 64      // threads per reduce workgroup (D/4 per query row)
@@ -552,7 +558,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // per page (which measured about 3% of the kernel time).  The segment is
   // then 256 pages, so that ids and scales fit the register budget.
   constexpr bool SEGSC = FP8 && PA_SEG_SCALES;
-  constexpr int kIdRegs = SEGSC ? 4 : 8;
+  // (four-tile BF16 kernels keep fewer ids, for registers to read Q ahead)
+  constexpr int kIdRegs = SEGSC ? 4 : (NQ == 4 ? PA_IDREGS4 : 8);
   constexpr int kSegPages = 64 * kIdRegs;
   int ids[kIdRegs];
   float sks[SEGSC ? kIdRegs : 1], svs[SEGSC ? kIdRegs : 1];
@@ -644,13 +651,15 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       for (int nq = 0; nq < NQ; ++nq)
         acc[nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qc[nq], acc[nq], 0, 0, 0);
     }
-#if PA_QK_SCHED
-    if constexpr (QLDS) {
-      // Keep PA_QK_SCHED LDS reads of Q ahead of the MFMAs that use them.  Left
-      // to itself the compiler waited for each read just before its MFMA,
+    constexpr int kAhead = NQ == 4 ? PA_QK_SCHED4 : PA_QK_SCHED;
+    if constexpr (QLDS && kAhead > 0) {
+      // Keep kAhead LDS reads of Q ahead of the MFMAs that use them.  Left to
+      // itself the compiler waited for each read just before its MFMA,
       // exposing the LDS latency 12 times per page (measured on MI355X: 17-19%
-      // of the prefill kernel's time); 5 or more ahead spill with BF16 pages.
-      constexpr int nr = NQ * NSTEP, ahead = PA_QK_SCHED;
+      // of the prefill kernel's time at 4 ahead, 9-11% more at 8 ahead with 4
+      // tiles).  With 2 tiles, 6 ahead spills in the page loop; with 4 BF16
+      // tiles, 8 ahead spills 5 registers that live only outside it.
+      constexpr int nr = NQ * NSTEP, ahead = kAhead;
       __builtin_amdgcn_sched_group_barrier(0x100, ahead, 0);
 #pragma unroll
       for (int i = 0; i < nr - ahead; ++i) {
@@ -659,7 +668,6 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       }
       __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
     }
-#endif
   };
 
   // Softmax update and O^T += V^T P^T for page k of the run, from its scores.
