@@ -28,6 +28,17 @@ constexpr float kRescaleSlack = 8.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int N> struct IntC { static constexpr int value = N; };   // a compile-time int argument
 
+// Max of four scores that are never NaN (masked ones are -inf), in two
+// v_max3_f32.  Written out because fmaxf must quiet NaN inputs first: the
+// compiler adds a canonicalising max for each operand it cannot prove
+// canonical (all of them after the causal mask's select).
+__device__ inline float max4(float a, float b, float c, float d) {
+  float t, r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(t) : "v"(a), "v"(b), "v"(c));
+  asm("v_max3_f32 %0, %1, %2, %2" : "=v"(r) : "v"(t), "v"(d));
+  return r;
+}
+
 // Tuning knobs (fixed at build time; the defaults are the measured best).
 #ifndef PA_PIPE_DEPTH
 #define PA_PIPE_DEPTH 2        // pages held in registers per wave (loads in flight + current)
@@ -671,7 +682,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   };
 
   // Softmax update and O^T += V^T P^T for page k of the run, from its scores.
-  auto pv = [&](const f32x4 (&acc)[NQ], const u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
+  auto pv = [&](const f32x4 (&acc)[NQ], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ksc;
@@ -699,7 +710,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
-      lmax[nq] = fmaxf(fmaxf(sc[nq][0], sc[nq][1]), fmaxf(sc[nq][2], sc[nq][3]));
+      lmax[nq] = max4(sc[nq][0], sc[nq][1], sc[nq][2], sc[nq][3]);
       grow |= lmax[nq] > m_run[nq] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -735,33 +746,33 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 
     // ---- O^T += V^T P^T; on the last page zero V of tokens past L (the
     // slots may hold anything, and 0 * NaN would poison the sum)
-    const bool vtail = page * kPageSize + kPageSize > L;
-    if (FP8) {
-      uint32_t vmask = 0xFFFFFFFFu;
-      if (vtail) {
-        const int nv = min(max(L - tok0, 0), 4);
-        vmask = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+    if (page * kPageSize + kPageSize > L) {   // the last page only, in place
+      const int nv = min(max(L - tok0, 0), 4);  // this lane's valid tokens (4 per dword row)
+      if (FP8) {
+        const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) vr[i] &= u32x4{m, m, m, m};
+      } else {   // BF16: tokens 0-1 in the even dwords, 2-3 in the odd ones
+        const uint64_t m = nv >= 4 ? ~0ull : ((1ull << (16 * nv)) - 1ull);
+        const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) vr[i] &= u32x4{lo, hi, lo, hi};
       }
+    }
+    if (FP8) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        uint32_t w = vr[j >> 2][j & 3];
-        if (vtail) w &= vmask;
+        const uint32_t w = vr[j >> 2][j & 3];
         const f16x4 vf = __builtin_bit_cast(f16x4, fp8x4_to_f16x4(w));
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
           o[nq][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pbh[nq], o[nq][j], 0, 0, 0);
       }
     } else {
-      uint64_t vmask = ~0ull;
-      if (vtail) {
-        const int nv = min(max(L - tok0, 0), 4);
-        vmask = nv >= 4 ? ~0ull : ((1ull << (16 * nv)) - 1ull);
-      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const u32x4& seg = vr[j >> 1];
-        uint64_t w = ((uint64_t)seg[2 * (j & 1) + 1] << 32) | seg[2 * (j & 1)];
-        if (vtail) w &= vmask;
+        const uint64_t w = ((uint64_t)seg[2 * (j & 1) + 1] << 32) | seg[2 * (j & 1)];
         const i16x4 vb = __builtin_bit_cast(i16x4, w);
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
@@ -770,8 +781,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  auto compute = [&](const u32x4 (&kr)[NSEG], const u32x4 (&vr)[NSEG], float ksc, float vsc,
-                     int k) {
+  auto compute = [&](const u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
     f32x4 acc[NQ];
     qk(acc, kr);
     pv(acc, vr, ksc, vsc, k);
