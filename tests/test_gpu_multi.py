@@ -89,10 +89,12 @@ def test_multi_column_tiles(cfg, heads, T, kw):
     run_case(w, partitions=(0, 1, 8))
 
 
-def test_multi_workload5_full_size_sampled():
-    """70B-shaped FP8 cache, L = 32768, T = 8 drafts: 64 columns per unit."""
-    w = make_workload(5, q_len=8)
-    run_case(w, seqs=[0, 37, 63], partitions=(8,), pools=False, fill_seqs=None)
+@pytest.mark.parametrize("T", [4, 8])
+def test_multi_workload5_full_size_sampled(T):
+    """70B-shaped FP8 cache, L = 32768, T = 4 or 8 drafts (32 or 64 columns per
+    unit): the automatic split the benchmark times (split-K 4) and split-K 8."""
+    w = make_workload(5, q_len=T)
+    run_case(w, seqs=[0, 37, 63], partitions=(0, 8), pools=False, fill_seqs=None)
 
 
 def test_multi_lengths_shorter_than_the_drafts():

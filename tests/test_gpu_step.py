@@ -95,3 +95,26 @@ def test_step_without_new_tokens_is_the_decode():
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     for got, want in zip(_state(dw.cache), before):
         assert torch.equal(got, want)
+
+
+def test_step_full_size_matches_append_then_decode():
+    """The 70B-shaped FP8 layer at full size (64 x 32K tokens, split-K 8, tag check
+    on), the benchmark's step: pa_decode_step against the two calls, bit for bit
+    (pools, scales, outputs, flags); the two calls are checked against the oracle
+    at this size in test_gpu_parity.py."""
+    w = make_workload(5)
+    dw = build_device_workload(w, log=log)
+    before = _state(dw.cache)
+    dw.step_append()
+    ref = dw.decode(check=True, num_partitions=8).clone()
+    torch.cuda.synchronize()
+    ref_flags = dw.flags.clone()
+    ref_state = _state(dw.cache)
+    _restore(dw.cache, before)
+    del before
+    out = dw.decode_step(check=True, num_partitions=8)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(dw.flags, ref_flags)
+    for got, want in zip(_state(dw.cache), ref_state):
+        assert torch.equal(got, want)
