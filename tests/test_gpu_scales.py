@@ -1,0 +1,72 @@
+"""Softmax scales other than 1/sqrt(D) on the GPU (the C ABI takes any finite one).
+
+A negative scale reverses the ranking of the scores, zero makes the weights
+uniform over the attended tokens, and a large one makes them nearly one-hot.
+Each is checked against the fp64 oracle run with the same scale, for plain
+decode (fixed and balanced splits), 4 drafts and a short prefill chunk, BF16
+and FP8.  Bars: those of the other parity tests (max-abs 1e-2, mean-abs 1e-3)
+where the output averages many rows (|o| well below 1); with the sharp scale an
+output is close to one V row (|o| up to about 4), and the kernel's two BF16
+roundings -- the weights P as MFMA operands and the output -- allow up to
+u * (|o| + max|V|) with u = 2^-8, so that is the per-element bar there (mean-abs
+still 1e-3); max|V| < 6.5 for these N(0, 1) draws.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_pa_amd import pa
+from decode_attention_paged_pa_amd.device_inputs import build_device_workload
+from decode_attention_paged_pa_amd.workloads import make_workload
+from oracle import oracle_decode, oracle_decode_multi
+from tests.oracle_fill import oracle_fill
+from tests.test_gpu_parity import MAX_ABS, MEAN_ABS, log, out_f64
+
+pytestmark = pytest.mark.gpu
+
+SCALES = (-1.0, 0.0, 4.0)   # multiples of the workload's own 1/sqrt(D)
+U_BF16 = 2.0 ** -8
+V_MAX = 6.5
+
+
+def _check(got, ref, what, sharp):
+    e = np.abs(got - ref)
+    log("%s: max-abs %.3g mean-abs %.3g" % (what, e.max(), e.mean()))
+    assert np.all(np.isfinite(got))
+    assert e.mean() <= MEAN_ABS, e.mean()
+    if sharp:
+        excess = e - U_BF16 * (np.abs(ref) + V_MAX)
+        assert excess.max() <= 0, excess.max()
+    else:
+        assert e.max() <= MAX_ABS, e.max()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_scales(kv):
+    w = make_workload(2, batch=4, lens=[1, 300, 1500, 4097], kv=kv, stale_frac=0.0)
+    dw = build_device_workload(w)
+    dw.step_append()
+    cache, _ = oracle_fill(w)
+    for f in SCALES:
+        sigma = float(np.float32(w.sigma * f))
+        ref = oracle_decode(cache, w.q, w.block_table, w.lens, sigma)
+        for parts in (0, 1, 5):
+            out = pa.decode(dw.cache, dw.q, dw.block_table, dw.lens, sigma, num_partitions=parts)
+            torch.cuda.synchronize()
+            _check(out_f64(out), ref, "%s decode scale %gx partitions %d" % (kv, f, parts),
+                   sharp=f > 1)
+
+
+@pytest.mark.parametrize("kv,T", [("fp8", 4), ("bf16", 16)])
+def test_multi_query_and_prefill_scales(kv, T):
+    w = make_workload(2, batch=3, lens=[20, 700, 2100], q_len=T, kv=kv, stale_frac=0.0)
+    dw = build_device_workload(w)
+    dw.step_append()
+    cache, _ = oracle_fill(w)
+    run = pa.decode_multi if T <= 8 else pa.prefill
+    for f in SCALES:
+        sigma = float(np.float32(w.sigma * f))
+        ref = oracle_decode_multi(cache, w.q, w.block_table, w.lens, sigma)
+        out = run(dw.cache, dw.q, dw.block_table, dw.lens, sigma)
+        torch.cuda.synchronize()
+        _check(out_f64(out), ref, "%s T=%d scale %gx" % (kv, T, f), sharp=f > 1)
