@@ -52,12 +52,14 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 4      // occupancy hint for the register allocator (0: none)
 #endif
-// Kernels with several query-column tiles: measured on MI355X, deeper rings
-// and dropping the throttle change nothing there (their time goes to compute
-// and to the lower occupancy), so they keep the same defaults.
 #ifndef PA_SEG_SCALES
 #define PA_SEG_SCALES 1        // FP8 scales gathered per segment with the page ids (else per page)
 #endif
+// Kernels with several query-column tiles: measured on MI355X, deeper rings
+// and dropping the throttle change nothing with two tiles (their time goes to
+// compute and to the lower occupancy), so those keep the same defaults; the
+// four-tile kernels hold one K buffer instead (PA_MQ_LATE_K), where the
+// compiler places the waits.
 #ifndef PA_MQ_PIPE_DEPTH
 #define PA_MQ_PIPE_DEPTH 2
 #endif
