@@ -284,6 +284,9 @@ def main():
                     help="split-K count (-1: 8 for the 70b-fp8-32k decode, else the library's "
                          "choice)")
     ap.add_argument("--no-check", action="store_true", help="no-op tracker: skip the tag check")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="keep this many KV heads (and their query heads) of the workload: one "
+                         "GPU's share of the layer when its KV heads are sharded over GPUs")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -332,7 +335,13 @@ def main():
         w = make_workload(2, batch=len(PREFILL_PREFIXES), stale_frac=0.0, q_len=C,
                           lens=np.array(PREFILL_PREFIXES) + C, table_width=2048)
     else:
-        w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len)
+        heads = None
+        if args.kv_heads > 0:
+            full = make_workload(args.config, stale_frac=0.0, batch=1)
+            if full.Hkv % args.kv_heads:
+                sys.exit("--kv-heads must divide the workload's %d KV heads" % full.Hkv)
+            heads = (full.G * args.kv_heads, args.kv_heads)
+        w = make_workload(args.config, stale_frac=0.0, q_len=args.q_len, heads=heads)
     # split-K 8 is the decode workload's own setting; multi-query steps take the
     # library's choice (whole grid resident: 4 on the 70B-shaped workload)
     parts = args.partitions if args.partitions >= 0 else (
@@ -459,7 +468,10 @@ def main():
         log("graph replay: step %.3f ms (%.0f GB/s)" % (g_ms, graph["value"]))
         del g
 
-    traffic = traffic_from_profile(w.name if T == 1 else "%s-t%d" % (w.name, T), None)
+    prof_name = w.name if T == 1 else "%s-t%d" % (w.name, T)
+    if args.kv_heads > 0:
+        prof_name += "-kv%d" % args.kv_heads
+    traffic = traffic_from_profile(prof_name, None)
     if args.prefill > 0:
         fl = prefill_flops(w)
         tflops = fl / (t_attn.mean() * 1e-3) / 1e12
@@ -511,7 +523,8 @@ def main():
                             n_parts if n_parts > 0 else "balanced on the device",
                             "on" if check else "off",
                             ("" if T == 1 else ", %d draft tokens per sequence (causal)" % T)
-                            + (", eviction scores updated" if args.scored else "")),
+                            + (", eviction scores updated" if args.scored else "")
+                            + (", one GPU's share of the KV heads" if args.kv_heads > 0 else "")),
             "q_len": T,
             "global_batch": w.B,
             "tokens_attended": int(w.lens.sum()),

@@ -52,6 +52,9 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 4      // occupancy hint for the register allocator (0: none)
 #endif
+#ifndef PA_VAL_PER
+#define PA_VAL_PER 8           // table entries per validation thread whose loads are issued together
+#endif
 #ifndef PA_SEG_SCALES
 #define PA_SEG_SCALES 1        // FP8 scales gathered per segment with the page ids (else per page)
 #endif
@@ -150,7 +153,23 @@ __device__ void validate_block(const ValidateArgs& a, int b) {
     }
     __syncthreads();
     const int total = s_off[nu];
-    constexpr int kPer = 8;
+    constexpr int kPer = PA_VAL_PER;
+    // With up to 8 units the offsets sit in registers and an entry's unit is a
+    // count of compares; more units search the LDS copy.
+    constexpr int kRegUnits = 8;
+    int offr[kRegUnits + 1];
+#pragma unroll
+    for (int k = 0; k <= kRegUnits; ++k) offr[k] = k <= nu ? s_off[k] : INT_MAX;
+    auto unit_of = [&](int i) {
+      int u = 0;
+      if (nu <= kRegUnits) {
+#pragma unroll
+        for (int k = 1; k <= kRegUnits; ++k) u += offr[k] <= i ? 1 : 0;
+      } else {
+        while (s_off[u + 1] <= i) ++u;
+      }
+      return u;
+    };
     for (int base = 0; base < total; base += kPer * 1024) {
       int pid[kPer];
       uint32_t want[kPer];
@@ -160,8 +179,7 @@ __device__ void validate_block(const ValidateArgs& a, int b) {
         pid[j] = 0;
         want[j] = 0u;
         if (i < total) {
-          int u = 0;
-          while (s_off[u + 1] <= i) ++u;          // the unit holding flat entry i
+          const int u = unit_of(i);               // the unit holding flat entry i
           const int row = a.head_layout ? b * a.num_kv_heads + u0 + u : b;
           const size_t e = (size_t)row * a.table_width + (i - s_off[u]);
           pid[j] = a.block_table[e];
