@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0: chunked prefill
+constexpr int kVersion = 500;  // 0.5.0: a decode step in one call (pa_decode_step)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
