@@ -284,8 +284,13 @@ __device__ void plan_block(const PlanArgs& a) {
     for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
     if (lane == 0) s_part[buf][wv] = (long long)v * hpg <= target ? 1 : 0;
     __syncthreads();
-    int w = 0;
-    while (w < 16 && s_part[buf][w] == 0) ++w;
+    // the first candidate that fits (16 if none): all 16 flags read at once
+    long long fit[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) fit[i] = s_part[buf][i];
+    int w = 16;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) w = fit[i] != 0 ? i : w;
     buf ^= 1;
     if (w == 0) {
       hi = lo;
