@@ -7,9 +7,10 @@
  *     when the cache is FP8;
  *   - pa_decode checks the page tags a request expects, then runs grouped-
  *     query attention of one query token per sequence over every cached token;
- * and around it: pa_decode_multi (speculative verification of up to 8 draft
- * tokens), pa_prefill (chunked prefill), pa_decode_scored (eviction scores)
- * and pa_cache_compact (compaction after eviction).
+ * and around it: pa_decode_step (a step's append and decode in one call),
+ * pa_decode_multi (speculative verification of up to 8 draft tokens),
+ * pa_prefill (chunked prefill), pa_decode_scored (eviction scores) and
+ * pa_cache_compact (compaction after eviction).
  *
  * Sources (web pages; the citations name the page title and the passage):
  *   [paging]  "How we built the most efficient inference engine for
