@@ -498,7 +498,8 @@ def main():
                            "reduce": round(t_red.mean() * 1e3, 2)},
             "roofline": {"bound": "mfma", "kernel": "attention_kernel", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_from_profile("llama8b-prefill-%d" % T, None)},
             "cpu_baseline": None}), flush=True)
         return
     result = {
