@@ -42,6 +42,14 @@ def test_prefill_headwise():
     run_case(w, partitions=(0, 16))
 
 
+def test_prefill_many_units_keep_index_order():
+    """More than 64 lengths (72 HEAD units): the launch keeps the index order
+    instead of starting the longest units first."""
+    lens = np.random.default_rng(7).integers(64, 700, size=(9, 8))
+    w = make_workload(4, lens=lens, q_len=64)
+    run_case(w, partitions=(0,))
+
+
 def test_prefill_short_chunks_equal_decode_multi_and_decode():
     w = make_workload(2, batch=3, lens=[9, 600, 2000], q_len=4)
     dw = build_device_workload(w)
