@@ -106,6 +106,33 @@ __device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
     uint16_t* kb = reinterpret_cast<uint16_t*>(a.k_pages) + blk * BLOCK_ELEMS;
     uint16_t* vb = reinterpret_cast<uint16_t*>(a.v_pages) +
                    v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
+    if (cnt == kPageSize && ((reinterpret_cast<uintptr_t>(a.k_new) |
+                              reinterpret_cast<uintptr_t>(a.v_new)) & 15) == 0) {
+      // A whole page from 16-byte aligned inputs (bulk and chunk appends):
+      // K rows keep runs of 32 dims of a token together, so 8 dims move as
+      // one 16-byte copy; V is stored token-minor, so a thread reads 4
+      // tokens x 8 dims and writes each dim's 4 tokens as 8 bytes.
+      for (int e = tid; e < kPageSize * D / 8; e += NTH) {
+        const int s = e / (D / 8), d = (e - s * (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(kb + k_elem<D, E>(s, d)) =
+            *reinterpret_cast<const u32x4*>(ks + s * D + d);
+      }
+      for (int e = tid; e < (kPageSize / 4) * (D / 8); e += NTH) {
+        const int tq = e / (D / 8), d0 = (e - tq * (D / 8)) * 8;
+        u32x4 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const u32x4*>(vs + (4 * tq + i) * D + d0);
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int sh = 16 * (dd & 1);
+          const uint32_t t0v = (r[0][dd >> 1] >> sh) & 0xFFFFu, t1v = (r[1][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t t2v = (r[2][dd >> 1] >> sh) & 0xFFFFu, t3v = (r[3][dd >> 1] >> sh) & 0xFFFFu;
+          *reinterpret_cast<u32x2*>(vb + v_elem<D, E>(4 * tq, d0 + dd)) =
+              u32x2{t0v | (t1v << 16), t2v | (t3v << 16)};
+        }
+      }
+      return;
+    }
     for (int e = tid; e < cnt * D; e += NTH) {
       const int s = e / D, d = e - s * D;
       kb[k_elem<D, E>(slot0 + s, d)] = ks[e];
