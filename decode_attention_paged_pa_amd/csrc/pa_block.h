@@ -55,11 +55,13 @@ __device__ __forceinline__ float bf16_value(uint16_t bits) { return __uint_as_fl
 // One append item: unit item / pages_per_unit and the j-th page counted from
 // the page holding the unit's first new token (the new tokens of several
 // pages of one unit are separate items).  NTH threads (whole waves; tid in
-// [0, NTH)) share the item, and s_red / s_old are theirs alone.  FP8 pages
-// keep scale = amax / 448 over everything written since the page started
-// (rules of the KV cache quantization paragraph, "How we built the most
-// efficient inference engine for Cloudflare's network"): the new tokens'
-// amax may raise it, and then the page's earlier codes are re-quantised.
+// [0, NTH)) share the item, and s_red / s_old are theirs alone.  The cache is
+// stored as FP8 e4m3 ("Cloudflare quantizes Kimi and GLM caches for 41%
+// faster inference", KV cache quantization paragraph); that page gives no
+// scale formula, and the rule used here is this library's reading: each FP8
+// page-head keeps scale = amax / 448 (448 being e4m3's largest finite value)
+// over everything written since the page started.  The new tokens' amax may
+// raise it, and then the page's earlier codes are re-quantised.
 //
 // Every thread passes the FP8 path's one barrier exactly once, whether or not
 // its item writes anything (inactive items, items past the unit's last page,

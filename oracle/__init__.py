@@ -14,7 +14,9 @@ Pins (tests/test_oracle_*.py) tie every function to something other than
 itself: exhaustive or brute-force codec checks, a library conversion,
 closed forms of attention, dense non-paged attention, page-permutation
 invariance, brute force at 50 digits on tiny shapes, the split/merge identity,
-and the scale invariant of the FP8 cache.  No function here is "parity
+the scale invariant of the FP8 cache, and the FP8 codes and scales bit for bit
+against a rebuild from exact rationals (one rounding to binary32 per named
+step, then the nearest e4m3 code by search).  No function here is "parity
 unpinned".
 """
 from .codecs import (  # noqa: F401

@@ -1,0 +1,414 @@
+"""Bit-level pin of the oracle's FP8 quantisation (CPU only).
+
+The FP8 KV cache ("Cloudflare quantizes Kimi and GLM caches for 41% faster
+inference", KV cache quantization paragraph) is written with a per-(page,
+head) scale s = fl32(amax / 448), codes RNE_e4m3(sat(fl32(x / s))), and, when
+a later append raises the scale from s_old to s_new, earlier codes become
+RNE_e4m3(sat(fl32(fl32(dec(c) * s_old) / s_new))).  Every rounding is named,
+so the codes are fixed bit for bit.
+
+This test rebuilds those codes from exact rationals, with no floating-point
+arithmetic at all: fractions.Fraction quotients and products, rounded once to
+binary32 by an explicit round-half-to-even rule on the exact value, then the
+nearest e4m3 value found by search over the 127 non-negative finite codes
+(ties to the even code).  It checks the oracle's oracle_append against that
+rebuild on inputs chosen to sit next to e4m3 rounding boundaries (where a
+slip in the fp32 step changes a code) and on random pages.  It also plants
+two plausible slips in the oracle -- x * (1 / s) instead of x / s, and a
+re-quantisation that multiplies by fl32(s_old / s_new) -- and shows that the
+rebuild catches each.
+"""
+import bisect
+import functools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.paged as paged
+from decode_attention_paged_pa_amd.workloads import to_bf16_bits
+from oracle import OracleCache, bf16_to_f64, e4m3_to_f64, oracle_append
+
+S, D = 16, 64
+
+
+# ------------------------------------------------------------ exact rebuild
+def f32_round(r):
+    """Exact rational -> the nearest binary32 value (as a Fraction), ties to even.
+
+    binary32: 24-bit significands; normal exponents -126..127; below 2^-126
+    the grid is 2^-149 (subnormals).  Values here stay far below the overflow
+    threshold.
+    """
+    if r == 0:
+        return Fraction(0)
+    neg = r < 0
+    a = -r if neg else r
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    v = lo * ulp
+    assert v < Fraction(2) ** 128
+    return -v if neg else v
+
+
+def e4m3_value(c):
+    """Exact value of a non-negative finite OCP e4m3 code (0 .. 126)."""
+    e, m = c >> 3, c & 7
+    if e == 0:
+        return Fraction(m, 8) * Fraction(1, 64)
+    return (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+E4M3_EXACT = [e4m3_value(c) for c in range(127)]
+
+
+def e4m3_nearest(v):
+    """Saturate |v| at 448, then the nearest code by search, ties to the even code;
+    a negative value keeps its sign bit, also when it rounds to zero.  The 127
+    values increase with the code, so a bisection finds the two neighbours."""
+    neg = v < 0
+    a = min(-v if neg else v, Fraction(448))
+    hi = min(max(bisect.bisect_left(E4M3_EXACT, a), 1), 126)
+    lo = hi - 1
+    dlo, dhi = a - E4M3_EXACT[lo], E4M3_EXACT[hi] - a
+    c = lo if dlo < dhi else hi if dhi < dlo else (lo if lo % 2 == 0 else hi)
+    return c | (0x80 if neg else 0)
+
+
+def e4m3_decode(c):
+    """Exact value of any finite code (sign bit 0x80)."""
+    v = E4M3_EXACT[c & 0x7F]
+    return -v if c & 0x80 else v
+
+
+def exact_scale(amax):
+    return f32_round(Fraction(float(amax)) / 448)
+
+
+@functools.lru_cache(maxsize=None)
+def _exact_code(x, s):
+    if s == 0:
+        return 0
+    return e4m3_nearest(f32_round(x / s))
+
+
+def exact_code(x, s):
+    return _exact_code(Fraction(float(x)), s)
+
+
+def exact_requant(c, s_old, s_new):
+    back = f32_round(e4m3_decode(int(c)) * s_old)
+    return _exact_code(back, s_new)
+
+
+# ------------------------------------------------------- input selection
+# The search below only picks inputs that sit next to e4m3 rounding
+# boundaries; the expected codes come from the exact rebuild above.
+POS_BF16 = np.arange(0x0080, 0x7F80, dtype=np.uint16)           # positive normal bf16 values
+POS_BF16_F32 = bf16_to_f64(POS_BF16).astype(np.float32)
+E4M3_SORTED = np.array([float(x) for x in E4M3_EXACT])
+
+
+def _nearest_code_np(q):
+    """Vectorised nearest-code search (selection only): ties to the even code."""
+    a = np.minimum(np.abs(q.astype(np.float64)), 448.0)
+    hi = np.clip(np.searchsorted(E4M3_SORTED, a), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - E4M3_SORTED[lo], E4M3_SORTED[hi] - a
+    return np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+
+
+def boundary_quotient_cases(n_scales=400, per_scale=2, seed=11):
+    """(amax, x) bf16 pairs, |x| <= amax, where fl32(x / s) and fl32(x * fl32(1 / s))
+    give different codes (s = fl32(amax / 448))."""
+    rng = np.random.default_rng(seed)
+    out = []
+    amaxes = POS_BF16_F32[rng.integers(0x3000, 0x5000, size=n_scales)]
+    for amax in amaxes:
+        s = np.float32(amax / np.float32(448.0))
+        xs = POS_BF16_F32[POS_BF16_F32 <= amax]
+        q1 = xs / s
+        q2 = xs * np.float32(np.float32(1.0) / s)
+        diff = np.nonzero(_nearest_code_np(q1) != _nearest_code_np(q2))[0]
+        for i in diff[:per_scale]:
+            out.append((np.float32(amax), xs[i]))
+    return out
+
+
+def _slip_ratio(dec, s_old, s_new):
+    return dec * np.float32(s_old / s_new)
+
+
+def _slip_once(dec, s_old, s_new):
+    return (dec.astype(np.float64) * np.float64(s_old) / np.float64(s_new)).astype(np.float32)
+
+
+def boundary_requant_cases(n_pairs=3000, seed=12, slip=_slip_ratio):
+    """(amax_old, amax_new, code) where the double rounding of the re-quantisation
+    and a slip (by default a multiplication by fl32(s_old / s_new)) give
+    different codes."""
+    rng = np.random.default_rng(seed)
+    codes = np.arange(1, 127)
+    out = []
+    for _ in range(n_pairs):
+        a_old = POS_BF16_F32[rng.integers(0x3800, 0x4800)]
+        a_new = POS_BF16_F32[rng.integers(0x3800, 0x4A00)]
+        if not a_new > a_old:
+            continue
+        s_old = np.float32(a_old / np.float32(448.0))
+        s_new = np.float32(a_new / np.float32(448.0))
+        if not s_new > s_old:
+            continue
+        dec = E4M3_SORTED[codes].astype(np.float32)
+        good = _nearest_code_np((dec * s_old).astype(np.float32) / s_new)
+        bad = _nearest_code_np(slip(dec, s_old, s_new))
+        for i in np.nonzero(good != bad)[0][:1]:
+            out.append((a_old, a_new, int(codes[i])))
+    return out
+
+
+def _bf16(x):
+    return to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _x_with_code(c, s_old, rng):
+    """A bf16 value whose code under s_old is c (searched among neighbours of
+    dec(c) * s_old), or None."""
+    target = float(E4M3_SORTED[c]) * float(s_old)
+    bits = int(_bf16(np.float32(target)).item())
+    for cand in [bits] + [bits + d for d in (-1, 1, -2, 2, -3, 3)]:
+        if not 0x0080 <= cand < 0x7F80:
+            continue
+        x = float(bf16_to_f64(np.uint16(cand)))
+        if exact_code(x, exact_scale_f(s_old)) == c:
+            return np.uint16(cand)
+    return None
+
+
+def exact_scale_f(s):
+    return Fraction(float(s))
+
+
+# -------------------------------------------------------------- the check
+def check_fresh_pages(cases, rng):
+    """Fresh pages of D-dim tokens, one (amax, x) case per page: slot 0 holds the
+    amax element (so the page's scale is exact_scale(amax)), the other slots
+    hold x, -x and random values below amax.  Returns the number of codes or
+    scales that differ from the exact rebuild."""
+    n = len(cases)
+    cache = OracleCache("seq", "fp8", n, S, 1, D)
+    bt = np.arange(n, dtype=np.int32)[:, None]
+    vals = np.zeros((n, 1, S, D), np.float32)
+    for i, (amax, x) in enumerate(cases):
+        v = rng.uniform(-1, 1, size=(S, D)).astype(np.float32) * amax
+        v[0, 0] = amax
+        v[1, :] = x
+        v[2, :] = -x
+        vals[i, 0] = v
+    bits = _bf16(vals)
+    zero = np.zeros(n, np.int32)
+    cnt = np.full(n, S, np.int32)
+    oracle_append(cache, bt, zero, cnt, bits, bits, 1)
+    bad = 0
+    for i in range(n):
+        xs = bf16_to_f64(bits[i, 0])
+        amax = np.max(np.abs(xs))
+        s = exact_scale(amax)
+        bad += Fraction(float(cache.k_scale[i, 0])) != s
+        # the amax element, x and -x (constant along the row), and a sample of
+        # the random slots
+        picks = [(0, 0), (1, 0), (2, 0), (1, D - 1)]
+        picks += [(int(t), int(d)) for t, d in zip(rng.integers(3, S, 8), rng.integers(0, D, 8))]
+        for t, d in picks:
+            bad += int(cache.k[i, 0, t, d]) != exact_code(xs[t, d], s)
+            bad += int(cache.v[i, 0, t, d]) != exact_code(xs[t, d], s)
+    return bad
+
+
+def check_requant(cases, rng):
+    """Pages filled by two appends: slot 0 the old amax, slot 1 a value of code c
+    under the old scale; then slot 2 the new, larger amax.  The first two
+    slots are re-quantised.  Returns the number of mismatched codes/scales."""
+    pages = []
+    for (a_old, a_new, c) in cases:
+        s_old = np.float32(float(exact_scale(a_old)))
+        xc = _x_with_code(c, s_old, rng)
+        if xc is not None and bf16_to_f64(xc) <= a_old:   # a_old stays the amax
+            pages.append((a_old, a_new, xc))
+    assert len(pages) >= 5, len(pages)
+    n = len(pages)
+    cache = OracleCache("seq", "fp8", n, S, 1, D)
+    bt = np.arange(n, dtype=np.int32)[:, None]
+    first = np.zeros((n, 1, 2, D), np.uint16)
+    second = np.zeros((n, 1, 1, D), np.uint16)
+    for i, (a_old, a_new, xc) in enumerate(pages):
+        first[i, 0, 0, :] = _bf16(np.full(D, a_old, np.float32))
+        first[i, 0, 1, :] = xc
+        second[i, 0, 0, :] = _bf16(np.full(D, -a_new, np.float32))
+    oracle_append(cache, bt, np.zeros(n, np.int32), np.full(n, 2, np.int32), first, first, 1)
+    oracle_append(cache, bt, np.full(n, 2, np.int32), np.ones(n, np.int32), second, second, 1)
+    bad = 0
+    for i, (a_old, a_new, xc) in enumerate(pages):
+        s_old = exact_scale(bf16_to_f64(first[i, 0, 0, 0]))
+        s_new = exact_scale(abs(bf16_to_f64(second[i, 0, 0, 0])))
+        bad += Fraction(float(cache.k_scale[i, 0])) != s_new
+        for slot in (0, 1):
+            c_first = exact_code(bf16_to_f64(first[i, 0, slot, 0]), s_old)
+            bad += int(cache.k[i, 0, slot, 0]) != exact_requant(c_first, s_old, s_new)
+        bad += int(cache.k[i, 0, 2, 0]) != exact_code(bf16_to_f64(second[i, 0, 0, 0]), s_new)
+    return bad
+
+
+# ------------------------------------------------------------ planted slips
+def _quantise_reciprocal(values_f32, scale):
+    """Planted slip: x * fl32(1 / s) in place of fl32(x / s)."""
+    if scale == 0:
+        return np.zeros(values_f32.shape, np.uint8)
+    r = np.float32(np.float32(1.0) / np.float32(scale))
+    return paged.e4m3_from_f32_rne_sat((values_f32.astype(np.float32) * r).astype(np.float32))
+
+
+def _append_page_ratio(pool, scales, pid, ph, first_slot, slots, new_bits):
+    """Planted slip: re-quantise as dec(c) * fl32(s_old / s_new), one multiply."""
+    x = bf16_to_f64(new_bits).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s_cand = np.float32(amax / np.float32(448.0))
+    s_old = np.float32(0) if first_slot == 0 else scales[pid, ph]
+    s_new = max(s_old, s_cand)
+    if s_new > s_old and first_slot > 0:
+        old = e4m3_to_f64(pool[pid, ph, :first_slot]).astype(np.float32)
+        ratio = np.float32(s_old / s_new)
+        pool[pid, ph, :first_slot] = paged.e4m3_from_f32_rne_sat((old * ratio).astype(np.float32))
+    pool[pid, ph, slots] = paged._quantise(x, s_new)
+    scales[pid, ph] = s_new
+
+
+def _append_page_once(pool, scales, pid, ph, first_slot, slots, new_bits):
+    """Planted slip: re-quantise with one rounding, fl32(dec(c) * s_old / s_new)
+    from a wider intermediate, instead of the two fp32 roundings."""
+    x = bf16_to_f64(new_bits).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s_cand = np.float32(amax / np.float32(448.0))
+    s_old = np.float32(0) if first_slot == 0 else scales[pid, ph]
+    s_new = max(s_old, s_cand)
+    if s_new > s_old and first_slot > 0:
+        old = e4m3_to_f64(pool[pid, ph, :first_slot])
+        once = (old * np.float64(s_old) / np.float64(s_new)).astype(np.float32)
+        pool[pid, ph, :first_slot] = paged.e4m3_from_f32_rne_sat(once)
+    pool[pid, ph, slots] = paged._quantise(x, s_new)
+    scales[pid, ph] = s_new
+
+
+# ------------------------------------------------------------------- tests
+def test_exact_rounding_helpers():
+    """The rebuild's own rounding rules on values whose answers are known."""
+    assert f32_round(Fraction(1, 3)) == Fraction(11184811, 2 ** 25)     # 0x3EAAAAAB
+    assert f32_round(Fraction(1) + Fraction(1, 2 ** 24)) == 1               # tie -> even
+    assert f32_round(Fraction(1) + Fraction(3, 2 ** 24)) == 1 + Fraction(1, 2 ** 22)
+    assert f32_round(Fraction(1, 2 ** 150)) == 0                            # half the least subnormal, tie -> 0
+    assert f32_round(Fraction(3, 2 ** 151)) == Fraction(1, 2 ** 149)
+    assert e4m3_nearest(Fraction(1) + Fraction(1, 16)) == 0x38              # tie between 1 and 1.125 -> 1 (even)
+    assert e4m3_nearest(Fraction(1) + Fraction(3, 16)) == 0x3A              # tie between 1.125 and 1.25 -> 1.25
+    assert e4m3_nearest(Fraction(500)) == 0x7E and e4m3_nearest(Fraction(-500)) == 0xFE
+    assert e4m3_nearest(Fraction(-1, 2 ** 11)) == 0x80                      # sign kept on underflow
+    assert e4m3_nearest(Fraction(3, 2 ** 10)) == 0x02                       # 1.5 steps of 2^-9: tie -> 2 (even)
+    assert e4m3_nearest(Fraction(1, 2 ** 10)) == 0x00                       # half a step: tie -> 0 (even)
+    assert e4m3_nearest(Fraction(3, 2 ** 11)) == 0x01                       # 0.75 of a step -> 1
+
+
+def test_fresh_page_codes_bit_exact_at_rounding_boundaries():
+    cases = boundary_quotient_cases()
+    assert len(cases) >= 20, len(cases)       # the search found boundary inputs
+    rng = np.random.default_rng(5)
+    assert check_fresh_pages(cases, rng) == 0
+
+
+def test_fresh_page_codes_bit_exact_random():
+    rng = np.random.default_rng(6)
+    amax = bf16_to_f64(_bf16(np.exp(rng.uniform(-8, 8, size=24)).astype(np.float32)))
+    cases = [(np.float32(a), np.float32(a * rng.uniform(0, 1))) for a in amax]
+    assert check_fresh_pages(cases, rng) == 0
+
+
+def test_requantisation_bit_exact_at_rounding_boundaries():
+    cases = boundary_requant_cases()
+    assert len(cases) >= 10, len(cases)
+    assert check_requant(cases, np.random.default_rng(7)) == 0
+
+
+def test_planted_reciprocal_division_is_caught(monkeypatch):
+    cases = boundary_quotient_cases()
+    monkeypatch.setattr(paged, "_quantise", _quantise_reciprocal)
+    assert check_fresh_pages(cases, np.random.default_rng(5)) > 0
+
+
+def test_planted_single_rounding_requant_is_caught(monkeypatch):
+    cases = boundary_requant_cases()
+    monkeypatch.setattr(paged, "_append_fp8_page", _append_page_ratio)
+    assert check_requant(cases, np.random.default_rng(7)) > 0
+
+
+def test_planted_single_rounding_from_wide_intermediate_is_caught(monkeypatch):
+    cases = boundary_requant_cases(n_pairs=30000, slip=_slip_once)   # rarer than the ratio slip
+    assert len(cases) >= 20, len(cases)
+    assert check_requant(cases, np.random.default_rng(8)) == 0      # the oracle itself
+    monkeypatch.setattr(paged, "_append_fp8_page", _append_page_once)
+    assert check_requant(cases, np.random.default_rng(8)) > 0
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_append_sequences_bit_exact(seed):
+    """Random append runs (bulk, 1-token, crossing pages, scale growth and
+    fresh restarts): every code and scale equals the rebuild that replays the
+    rules on exact rationals, page by page."""
+    rng = np.random.default_rng(100 + seed)
+    P, W = 6, 6
+    cache = OracleCache("seq", "fp8", P, S, 1, 8)
+    bt = rng.permutation(P).astype(np.int32)[None, :W]
+    state = {}                                     # pid -> (scale Fraction, [codes per slot])
+    L = 0
+    for step in range(14):
+        n = int(rng.integers(1, 21))
+        n = min(n, W * S - L)
+        if n == 0:
+            break
+        mag = np.exp(rng.uniform(-2, 2))
+        x = (rng.standard_normal((1, 1, n, 8)) * mag).astype(np.float32)
+        bits = _bf16(x)
+        oracle_append(cache, bt, np.array([L], np.int32), np.array([n], np.int32), bits, bits, W)
+        t = 0
+        while t < n:                                # the rules, page by page, on rationals
+            pos = L + t
+            i, slot0 = pos // S, pos % S
+            cnt = min(S - slot0, n - t)
+            pid = int(bt[0, i])
+            xs = bf16_to_f64(bits[0, 0, t:t + cnt])
+            s_cand = exact_scale(np.max(np.abs(xs)))
+            if slot0 == 0:
+                s_old, codes = Fraction(0), [None] * S
+            else:
+                s_old, codes = state[pid]
+            s_new = max(s_old, s_cand)
+            if s_new > s_old and slot0 > 0:
+                for sl in range(slot0):
+                    codes[sl] = [exact_requant(c, s_old, s_new) for c in codes[sl]]
+            for j in range(cnt):
+                codes[slot0 + j] = [exact_code(v, s_new) for v in xs[j]]
+            state[pid] = (s_new, codes)
+            t += cnt
+        L += n
+    for pid, (s, codes) in state.items():
+        assert Fraction(float(cache.k_scale[pid, 0])) == s
+        for sl, cs in enumerate(codes):
+            if cs is not None:
+                assert [int(c) for c in cache.k[pid, 0, sl]] == cs, (pid, sl)
