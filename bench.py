@@ -12,19 +12,23 @@ Default workload: the 70B-shaped FP8 layer, B 64, 64 query / 8 KV heads,
 D 128, 32768 tokens per sequence (4.29 GB of FP8 KV), split-K 8, tag check on.
 
 Timing: W untimed warm-up steps; then K steps, each preceded (outside the
-timed events) by a 512 MiB write that evicts L2 and the Infinity Cache; HIP
-events on the launch stream bracket each step.  The K steps are also
+timed events) by a 1 GiB write that evicts L2 and the 256 MB Infinity Cache;
+HIP events on the launch stream bracket each step.  The K steps are also
 bracketed by device synchronisation for a wall-clock figure.  A second pass
 of K steps records events between the kernels as well, for the per-kernel
 split and the attention kernel's roofline (an event between two kernels
 costs a few microseconds itself, so the timed steps carry none).
 
 Prints one JSON line.  `value` is the achieved HBM GB/s of the step
-(algorithmic bytes / mean step time); `roofline` is the attention kernel
-against the 8 TB/s HBM peak; `cpu_baseline` is the fp64 oracle's decode on a
-bounded sample of the same workload, on this host's cores.  `graph` is the
-same step captured once as a HIP graph and replayed K times (one graph launch
-per step instead of three kernel launches).
+(algorithmic bytes / mean step time; `step_ms` adds the median, p10 and p90);
+`roofline` is the attention kernel against the 8 TB/s HBM peak;
+`measured_ceiling` is what this GPU reads per second with the library's read
+probes (pa_probe.h: a 4 GiB contiguous stream, and gathers of random 2 KiB
+blocks), and the attention kernel's share of the gather ceiling;
+`cpu_baseline` is the fp64 oracle's decode on a bounded sample of the same
+workload, on this host's cores.  `graph` is the same step captured once as a
+HIP graph and replayed K times (one graph launch per step instead of three
+kernel launches).  --ceiling-only runs the probes alone.
 
 --q-len T (2..8) turns the step into a multi-query step (speculative
 verification): the append writes T draft tokens per unit and
@@ -49,6 +53,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30           # write before each timed step: evicts L2 and the Infinity Cache
+CEILING_BYTES = 4 << 30         # the read probes' buffer
+CPU_WORKERS = 16                # the host cores one GPU's share of the box gives the oracle
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_PREFIXES = (0, 2048, 8192, 30720)
 
@@ -153,7 +160,8 @@ def cpu_baseline(w, n_seqs):
     import multiprocessing as mp
 
     ctx = mp.get_context("spawn")
-    cores = max(1, min(16, len(os.sched_getaffinity(0)), n_seqs))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(CPU_WORKERS, affinity, n_seqs))
     step = max(1, w.B // n_seqs)
     sample = list(range(0, w.B, step))[:n_seqs]
     shares = [sample[i::cores] for i in range(cores)]
@@ -184,12 +192,87 @@ def cpu_baseline(w, n_seqs):
     except Exception:
         pass
     fn = "oracle_decode" if w.q_len == 1 else "oracle_decode_multi (%d drafts)" % w.q_len
+    per = sorted(set(len(x) for x in shares))
     return dict(value=len(sample) * w.q_len / wall, unit="tokens/s", cores=cores, kind="oracle",
                 sample="%s (gather, FP8 dequant, fp64 attention) of %d of the %d "
-                       "sequences (all %d query heads each) of the same workload, one per worker, "
-                       "cache build untimed; %.1f s of CPU decode work; %s" % (
-                           fn, len(sample), w.B, w.Hq, sum(times), cpu_model),
-                seconds_wall=wall)
+                       "sequences (all %d query heads each) of the same workload, %s per worker "
+                       "process (one thread each), cache build untimed; %.1f s of CPU decode "
+                       "work; %s" % (fn, len(sample), w.B, w.Hq,
+                                     " or ".join(str(x) for x in per), sum(times), cpu_model),
+                seconds_wall=wall, host_affinity_cores=affinity,
+                cores_note="%d worker processes: one GPU's share of the box's host cores "
+                           "(%d visible to the process)" % (cores, affinity))
+
+
+# ---------------------------------------------------------------- read ceiling
+def _timed(fn, stream, flush, reps):
+    """Median ms of `reps` calls of fn, each after the flush write, by HIP events."""
+    import numpy as np
+    import torch
+
+    ts = []
+    for _ in range(reps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def measure_ceilings(dev, flush, reps=5, log_fn=None):
+    """What this GPU reads per second (pa_probe.h), best over the probes' launch shapes:
+    a contiguous read of CEILING_BYTES; a gather of every 2 KiB block of that
+    buffer in random order (2048 waves, one run of blocks each); and the
+    decode's own SEQ pattern, pages of 8 head blocks (16 KiB) in random order
+    whose 8 blocks are read by 8 waves on one XCD."""
+    import numpy as np
+    import torch
+
+    from decode_attention_paged_pa_amd import pa
+
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    out = {}
+    best = (0.0, None)
+    for waves in (2048, 8192, 16384):
+        ms = _timed(lambda: pa.probe_stream(buf, waves, sink, stream), stream, flush, reps)
+        gbs = CEILING_BYTES / (ms * 1e-3) / 1e9
+        best = max(best, (gbs, "%d waves" % waves))
+    out["stream_read"] = {"GB/s": round(best[0], 1), "bytes": CEILING_BYTES, "config": best[1]}
+    rng = np.random.default_rng(99)
+    nblk = CEILING_BYTES // 2048
+    waves = 2048
+    # random 2 KiB blocks, every block once
+    ids = torch.from_numpy(rng.permutation(nblk).astype(np.int32).reshape(waves, -1)).to(dev)
+    # SEQ pages: 8 consecutive 2 KiB blocks (one per KV head) in random page order; the
+    # 8 waves of a page run are the 4 waves of workgroups x and x + 8 (one XCD)
+    npg = nblk // 8
+    runs = waves // 8
+    order = rng.permutation(npg).astype(np.int64).reshape(runs, -1)
+    page_ids = np.empty((waves, order.shape[1]), np.int32)
+    for r in range(runs):
+        for h in range(8):
+            wg = (r // 8) * 16 + (h // 4) * 8 + r % 8
+            page_ids[wg * 4 + h % 4] = (order[r] * 8 + h).astype(np.int32)
+    page_ids = torch.from_numpy(page_ids).to(dev)
+    for name, tab in (("gather_2KiB", ids), ("gather_2KiB_seq_pages", page_ids)):
+        best = (0.0, None)
+        for inflight in (1, 2, 4):
+            ms = _timed(lambda: pa.probe_gather(buf, tab, waves, 2048, inflight, sink, stream),
+                        stream, flush, reps)
+            gbs = (nblk * 2048 + nblk * 4) / (ms * 1e-3) / 1e9
+            if log_fn:
+                log_fn("%s inflight %d: %.3f ms, %.0f GB/s" % (name, inflight, ms, gbs))
+            best = max(best, (gbs, "%d waves, %d blocks in flight per wave" % (waves, inflight)))
+        out[name] = {"GB/s": round(best[0], 1), "bytes": nblk * 2048 + nblk * 4, "config": best[1]}
+    del buf, ids, page_ids
+    torch.cuda.synchronize()
+    return out
 
 
 # ---------------------------------------------------------------- compaction
@@ -239,7 +322,7 @@ def bench_compaction(args):
     n_keep_d = torch.from_numpy(n_keep.astype(np.int32)).cuda()
     nt_d = torch.from_numpy(nt).cuda()
     scores = dw.cache.new_scores()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     for _ in range(args.warmup):
         pa.compact(dw.cache, dw.block_table, dw.lens, keep_d, n_keep_d, nt_d, scores=scores)
     torch.cuda.synchronize()
@@ -303,6 +386,9 @@ def main():
                     help="time a chunked-prefill step with this chunk length instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only run the HBM read probes (pa_probe.h) and print their rates")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read probes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -327,6 +413,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
+    if args.ceiling_only:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        c = measure_ceilings(dev, flush, log_fn=log)
+        print(json.dumps({"metric": "HBM read ceiling (pa_probe.h)", "measured_ceiling": c,
+                          "peak": HBM_PEAK_GBS}), flush=True)
         return
     if args.compact > 0:
         return bench_compaction(args)
@@ -366,7 +458,7 @@ def main():
         ws_bytes = pa.multi_workspace_bytes(dw.cache, dw.block_table, dw.lens, w.Hq, T, parts)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty(tuple(dw.q.shape), dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     # a decode step is pa_decode_step (its append shares the validation's launch),
@@ -532,6 +624,9 @@ def main():
             "parallelism": "1 GPU",
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(t_step)), 4),
+                    "p10": round(float(np.percentile(t_step, 10)), 4),
+                    "p90": round(float(np.percentile(t_step, 90)), 4)},
         "tokens_per_s": round(tok_s, 1),
         "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
         "ms_per_step_with_kernel_events": round(float(t_split.mean()), 4),
@@ -554,6 +649,16 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_ceiling and args.prefill == 0:
+        c = measure_ceilings(dev, flush, log_fn=log)
+        c["attention_pct_of_gather_ceiling"] = round(
+            100 * attn_gbs / max(c["gather_2KiB"]["GB/s"], c["gather_2KiB_seq_pages"]["GB/s"]), 2)
+        c["attention_pct_of_stream_ceiling"] = round(100 * attn_gbs / c["stream_read"]["GB/s"], 2)
+        result["measured_ceiling"] = c
+        log("read ceiling: stream %.0f GB/s, 2 KiB gather %.0f GB/s, SEQ-page gather %.0f GB/s; "
+            "attention at %.1f%% of the best gather" % (
+                c["stream_read"]["GB/s"], c["gather_2KiB"]["GB/s"],
+                c["gather_2KiB_seq_pages"]["GB/s"], c["attention_pct_of_gather_ceiling"]))
     del flush, workspace
     if not args.no_cpu_baseline:
         log("timing the oracle on %d sequences ..." % args.cpu_seqs)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpa.so")
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_append.hip", "pa_evict.hip"]
+SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_append.hip", "pa_evict.hip", "pa_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

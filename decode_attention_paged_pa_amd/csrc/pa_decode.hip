@@ -25,6 +25,14 @@ namespace {
 // sums and f16/bf16 MFMA operands hold without loss of range.
 constexpr float kRescaleSlack = 8.0f;
 
+// FP8 P.V operands are f16: p * (v_scale / v_ref) * kPScale, where v_ref is
+// the largest V scale the wave has met so far in its run.  The factor is at
+// most 1 and p at most 2^8, so the operand stays below 2^15, inside f16's
+// range (65504) whatever the cache's magnitudes, and weights down to 2^-21
+// of the largest keep f16's full precision.  O then accumulates in units of
+// v_ref / kPScale, and is converted when partials or outputs are written.
+constexpr float kPScale = 128.0f;
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int N> struct IntC { static constexpr int value = N; };   // a compile-time int argument
 
@@ -54,9 +62,6 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #endif
 #ifndef PA_VAL_PER
 #define PA_VAL_PER 8           // table entries per validation thread whose loads are issued together
-#endif
-#ifndef PA_SEG_SCALES
-#define PA_SEG_SCALES 1        // FP8 scales gathered per segment with the page ids (else per page)
 #endif
 // Kernels with several query-column tiles: measured on MI355X, deeper rings
 // and dropping the throttle change nothing with two tiles (their time goes to
@@ -603,6 +608,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const uint8_t* vpool = a.v_pages + (HEAD ? 0 : (size_t)(v_rot ? (h + 1) % Hkv : h) * BLOCK);
   const float* kscale = FP8 ? a.k_scale + (HEAD ? 0 : h) : nullptr;
   const float* vscale = FP8 ? a.v_scale + (HEAD ? 0 : h) : nullptr;
+  float v_ref = 0.f;   // FP8: the reference V scale of the P.V operands (uniform; see kPScale)
   const int scale_stride = HEAD ? 1 : Hkv;
   const int lane_off = (c * 4 + q4) * 16;
 
@@ -618,8 +624,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // FP8 scales of the segment's pages are gathered the same way, one lane per
   // page, right after the ids: two gathers per 64 pages instead of two loads
   // per page (which measured about 3% of the kernel time).  The segment is
-  // then 256 pages, so that ids and scales fit the register budget.
-  constexpr bool SEGSC = FP8 && PA_SEG_SCALES;
+  // then 256 pages, so that ids and scales fit the register budget.  The
+  // segment's largest V scale updates the wave's reference scale there.
+  constexpr bool SEGSC = FP8;
   // (four-tile BF16 kernels keep fewer ids, for registers to read Q ahead)
   constexpr int kIdRegs = SEGSC ? 4 : (NQ == 4 ? PA_IDREGS4 : 8);
   constexpr int kSegPages = 64 * kIdRegs;
@@ -655,18 +662,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       kr[i] = load16(kp + lane_off + i * 1024);
       vr[i] = load16(vp + lane_off + i * 1024);
     }
-    if constexpr (SEGSC) {
+    if constexpr (SEGSC) {   // vsc: the page's V scale / v_ref * kPScale
       ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), r & 63));
       vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), r & 63));
-    } else if (FP8) {
-      // A per-lane zero the compiler cannot see through keeps these two loads
-      // on the vector path: they then complete in order with the page data,
-      // whereas scalar loads complete out of order and each wait for one
-      // would wait for all of them.
-      int zero = 0;
-      asm volatile("" : "+v"(zero));
-      ksc = kscale[(size_t)pid * scale_stride + zero];
-      vsc = vscale[(size_t)pid * scale_stride + zero];
     }
   };
 
@@ -841,8 +839,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // This wave's result for partition `part`: the normalised output when the
   // unit has a single partition, else the partial (max, sum, unnormalised O).
   // A column that saw no token (multi-query, L - T + t < 0) has sum 0 and
-  // O = 0, and is written as zeros.
-  auto emit = [&](int part) {
+  // O = 0, and is written as zeros.  vfac converts O to the values' units
+  // (FP8: v_ref / kPScale; 1 for BF16 and for a parked partition).
+  auto emit = [&](int part, float vfac) {
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const float l_tot = col_sum(l_acc[nq]);
@@ -854,7 +853,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             a.row_ml[qrow * 2 + 0] = m_run[nq];
             a.row_ml[qrow * 2 + 1] = l_tot;
           }
-          const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
+          const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : (FP8 ? vfac / l_tot : 1.f / l_tot);
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
             const f32x4 v = o[nq][j];
@@ -867,7 +866,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
           const size_t pi = planned ? (size_t)pslot * C + cc : qrow * Pn + part;
           float* po = a.part_o + pi * D;
 #pragma unroll
-          for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = o[nq][j];
+          for (int j = 0; j < NT; ++j)
+            *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = FP8 ? o[nq][j] * vfac : o[nq][j];
           if (q4 == 0) {
             a.part_ml[pi * 2 + 0] = m_run[nq];
             a.part_ml[pi * 2 + 1] = l_tot;
@@ -904,8 +904,27 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         sks[j] = kscale[(size_t)pid * scale_stride];
         svs[j] = vscale[(size_t)pid * scale_stride];
       }
-      int lastsc = __builtin_amdgcn_readfirstlane(__float_as_int(svs[kIdRegs - 1]));
-      asm volatile("" : : "s"(lastsc));
+      // The largest V scale of the segment's pages in this run; when it
+      // exceeds the reference, O moves to the new units (a rare rescale:
+      // once per wave for caches of one magnitude).  NaN scales are skipped
+      // here and still poison their own page's operands, as they should.
+      float vmax = 0.f;
+#pragma unroll
+      for (int j = 0; j < kIdRegs; ++j) vmax = seg + 64 * j + lane < n ? fmaxf(vmax, svs[j]) : vmax;
+      vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(vmax))));
+      if (vmax > v_ref) {
+        if (v_ref > 0.f) {
+          const float r = v_ref / vmax;
+#pragma unroll
+          for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) o[nq][j] *= r;
+        }
+        v_ref = vmax;
+      }
+      const float to_op = v_ref > 0.f ? kPScale / v_ref : 0.f;
+#pragma unroll
+      for (int j = 0; j < kIdRegs; ++j) svs[j] *= to_op;
     }
     id_chunk = 0;
     if constexpr (LATEK) {
@@ -947,11 +966,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
               // Park the finished partition in LDS: a global store now would
               // be waited for by the next page's throttle, and under the full
               // read stream stores take long to complete (measured: 6% of the
-              // kernel time on the 32K-token FP8 workload).
+              // kernel time on the 32K-token FP8 workload).  FP8 O is parked in
+              // the values' units: the reference scale may still grow.
+              const float vfac = FP8 ? v_ref / kPScale : 1.f;
 #pragma unroll
               for (int j = 0; j < NT; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[0][j][r];
+                for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[0][j][r] * vfac;
               stash[4 * NT][lane] = m_run[0];
               stash[4 * NT + 1][lane] = l_acc[0];
               ++part;
@@ -967,7 +988,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       }
     }
   }
-  emit(part);
+  emit(part, FP8 ? v_ref / kPScale : 1.f);
   if constexpr (NQ == 1) {
     if (part > part0) {  // the parked first partition
 #pragma unroll
@@ -976,7 +997,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         for (int r = 0; r < 4; ++r) o[0][j][r] = stash[4 * j + r][lane];
       m_run[0] = stash[4 * NT][lane];
       l_acc[0] = stash[4 * NT + 1][lane];
-      emit(part0);
+      emit(part0, 1.f);
     }
   }
 }

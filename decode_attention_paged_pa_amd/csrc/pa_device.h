@@ -87,6 +87,13 @@ __device__ inline float col_max(float x) {
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
+// Maximum over the 64 lanes of a wave (NaN inputs are ignored by fmaxf).
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
+  return x;
+}
+
 __device__ inline float col_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);

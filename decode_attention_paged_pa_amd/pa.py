@@ -121,6 +121,10 @@ def lib():
         L.pa_strerror.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
         L.pa_version.restype = ctypes.c_int
+        L.pa_probe_stream.argtypes = [vp, sz, i32, vp, vp]
+        L.pa_probe_stream.restype = ctypes.c_int
+        L.pa_probe_gather.argtypes = [vp, sz, vp, i32, i32, i32, i32, vp, vp]
+        L.pa_probe_gather.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -512,6 +516,32 @@ def _decode(cache, q, q_len, block_table, lens, softmax_scale, expected_tags, fl
     if rc != 0:
         raise PAError(rc, "pa_decode_multi" if q_len > 1 else "pa_decode")
     return out
+
+
+def probe_stream(buf, waves, sink, stream=None):
+    """HBM read probe (pa_probe.h): read the uint8 device buffer `buf` once."""
+    _need(buf, "buf", (torch.uint8,))
+    _need(sink, "sink", U32)
+    if sink.numel() < waves:
+        raise ValueError("sink needs %d words" % waves)
+    rc = lib().pa_probe_stream(_ptr(buf), buf.numel(), waves, _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise PAError(rc, "pa_probe_stream")
+
+
+def probe_gather(pool, ids, waves, block_bytes, inflight, sink, stream=None):
+    """HBM read probe (pa_probe.h): wave w reads the blocks ids[w] names."""
+    _need(pool, "pool", (torch.uint8,))
+    _need(ids, "ids", I32)
+    _need(sink, "sink", U32)
+    if ids.dim() != 2 or ids.shape[0] != waves:
+        raise ValueError("ids must be [waves][ids_per_wave]")
+    if sink.numel() < waves:
+        raise ValueError("sink needs %d words" % waves)
+    rc = lib().pa_probe_gather(_ptr(pool), pool.numel(), _ptr(ids), waves, ids.shape[1],
+                               block_bytes, inflight, _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise PAError(rc, "pa_probe_gather")
 
 
 def version():

@@ -36,6 +36,13 @@ Multi-query workloads (q_len T > 1, speculative verification) draw the same
 way with T in place of the single new token: per KV head a history of L - T
 tokens, then the T draft tokens; queries are [B][T][Hq][D], drawn in step 4
 instead of the [B][Hq][D] ones.  With T = 1 every draw is the one above.
+
+Magnitudes (kv_mag, for range tests of the FP8 cache): K and V may be
+multiplied, before the BF16 rounding, by a constant, by a factor drawn per
+logical page of each unit (10^U(lo, hi), "pages"), or by a factor that grows
+along the unit (10^(lo + (hi - lo) * page / pages), "ramp").  The factors come
+after all other draws of the sequence's stream, so the N(0, 1) draws are the
+same with or without them.
 """
 from dataclasses import dataclass, field
 
@@ -68,6 +75,7 @@ class Workload:
     seed: int = 0
     q_len: int = 1              # T: query (draft) tokens per sequence, the last T of each unit
     extra: dict = field(default_factory=dict)
+    kv_mag: dict = None         # {"k"|"v": float | ("pages"|"ramp", lo, hi)} magnitudes
 
     @property
     def G(self):
@@ -105,7 +113,32 @@ class Workload:
                 vh[h, :n] = rng.standard_normal((n, self.D), dtype=np.float32)
                 kn[h] = rng.standard_normal((T, self.D), dtype=np.float32)
                 vn[h] = rng.standard_normal((T, self.D), dtype=np.float32)
+        if self.kv_mag:
+            for which, (hist, new) in (("k", (kh, kn)), ("v", (vh, vn))):
+                spec = self.kv_mag.get(which)
+                if spec is None:
+                    continue
+                for h in range(self.Hkv):
+                    n = int(n_hist[h])
+                    f = _magnitudes(spec, n + T, self.S, rng)
+                    hist[h, :n] *= f[:n, None]
+                    new[h] *= f[n:, None]
         return (to_bf16_bits(kh), to_bf16_bits(vh), to_bf16_bits(kn), to_bf16_bits(vn), n_hist)
+
+
+def _magnitudes(spec, L, S, rng):
+    """Per-token fp32 factors of one unit of L tokens (see kv_mag)."""
+    if not isinstance(spec, tuple):
+        return np.full(L, spec, np.float32)
+    kind, lo, hi = spec
+    pages = max(-(-L // S), 1)
+    if kind == "pages":
+        e = rng.uniform(lo, hi, size=pages)
+    elif kind == "ramp":
+        e = lo + (hi - lo) * np.arange(pages) / max(pages - 1, 1)
+    else:
+        raise ValueError(kind)
+    return np.repeat((10.0 ** e).astype(np.float32), S)[:L]
 
 
 def to_bf16_bits(x):
@@ -120,7 +153,7 @@ CONFIG_NAMES = {1: "tiny", 2: "llama8b-bf16", 3: "llama8b-fp8-tags", 4: "headwis
 
 def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
                   spare_pages=64, table_width=None, q_len=1, heads=None, kv=None, layout=None,
-                  head_dim=None):
+                  head_dim=None, kv_mag=None, sigma=None):
     """Draw workload `cfg_id` (1..5).
 
     batch / lens / table_width override the workload's own sizes for reduced
@@ -130,7 +163,9 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     8 drafts; chunked prefill: a chunk of q_len prompt tokens);
     heads = (Hq, Hkv) overrides the head counts (edge cases of the grouping);
     kv ("bf16" | "fp8"), layout ("seq" | "head") and head_dim (64 | 128)
-    override the cache format, for the combinations no named workload uses.
+    override the cache format, for the combinations no named workload uses;
+    kv_mag scales K and V (see the module notes) and sigma overrides the
+    softmax scale 1/sqrt(D).
     The draws keep their order; their sizes follow the overridden shapes.
     """
     if int(q_len) < 1:
@@ -216,7 +251,8 @@ def make_workload(cfg_id, *, batch=None, lens=None, seed=None, stale_frac=None,
     return Workload(
         cfg_id=cfg_id, name=CONFIG_NAMES[cfg_id], layout=spec["layout"], kv_dtype=spec["kv"],
         B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, W=W, P=P,
-        sigma=np.float32(1.0 / np.sqrt(D)),
+        sigma=np.float32(1.0 / np.sqrt(D)) if sigma is None else np.float32(sigma),
         lens=L, block_table=block_table, page_tags=page_tags,
         expected_tags=exp_rows.reshape(block_table.shape),
-        stale=stale_rows.reshape(block_table.shape), q=q, seed=seed, q_len=int(q_len))
+        stale=stale_rows.reshape(block_table.shape), q=q, seed=seed, q_len=int(q_len),
+        kv_mag=kv_mag)

@@ -57,7 +57,7 @@ def dense_tokens(kv_b, layout, h):
     return K, V
 
 
-def oracle_sequence(w, b, with_mass=False):
+def oracle_sequence(w, b, with_mass=False, with_pools=True):
     """Oracle result of sequence b alone, on a compact local pool.
 
     The sequence's pages are renumbered 0..n-1 (the result does not depend on
@@ -65,7 +65,8 @@ def oracle_sequence(w, b, with_mass=False):
     Returns dict(pages=global page ids [n], k, v = local logical pools [n][H][S][D],
     k_scale, v_scale = [n][H] or None, out = fp64 [Hq][D], or [T][Hq][D] for a
     multi-query workload (unflagged result)); with_mass adds mass = {h: the
-    step's attention mass per token [L]} (decode workloads).
+    step's attention mass per token [L]} (decode workloads); without
+    with_pools the pools and scales are left out (None).
     """
     from oracle import oracle_attention_mass, oracle_decode, oracle_decode_multi
 
@@ -89,9 +90,11 @@ def oracle_sequence(w, b, with_mass=False):
         out = oracle_decode(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
     else:
         out = oracle_decode_multi(cache, w.q[b:b + 1], local, lens, w.sigma)[0]
-    r = dict(pages=pages, k=cache.k[:len(pages)], v=cache.v[:len(pages)],
-             k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
-             v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)], out=out)
+    r = dict(pages=pages, k=None, v=None, k_scale=None, v_scale=None, out=out)
+    if with_pools:
+        r.update(k=cache.k[:len(pages)], v=cache.v[:len(pages)],
+                 k_scale=None if cache.k_scale is None else cache.k_scale[:len(pages)],
+                 v_scale=None if cache.v_scale is None else cache.v_scale[:len(pages)])
     if with_mass:
         m = oracle_attention_mass(cache, w.q[b:b + 1], local, lens, w.sigma)
         r["mass"] = {h: m[(0, h)] for (_, h) in m}
@@ -113,16 +116,47 @@ class _SubWorkload:
         return self._w.seq_kv(self._b)
 
 
-def oracle_sequences_parallel(w, seqs, workers=None, with_mass=False):
-    """oracle_sequence for several sequences in a process pool."""
-    import multiprocessing
+def _workers(n):
     import os
+
+    return max(1, min(16, len(os.sched_getaffinity(0)), n))
+
+
+def _pool(workers):
+    import multiprocessing
     from concurrent.futures import ProcessPoolExecutor
 
-    workers = workers or max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
-    if workers == 1:
-        return {b: oracle_sequence(w, b, with_mass) for b in seqs}
     # spawn: a forked child of a process with live OpenMP/torch thread pools can deadlock
-    with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
-        return dict(zip(seqs, ex.map(oracle_sequence, [w] * len(seqs), seqs,
-                                     [with_mass] * len(seqs))))
+    return ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn"))
+
+
+def _run(ex, w, seqs, with_mass, with_pools):
+    n = len(seqs)
+    if ex is None:
+        return {b: oracle_sequence(w, b, with_mass, with_pools) for b in seqs}
+    return dict(zip(seqs, ex.map(oracle_sequence, [w] * n, seqs, [with_mass] * n,
+                                 [with_pools] * n)))
+
+
+def oracle_sequences_parallel(w, seqs, workers=None, with_mass=False, with_pools=True):
+    """oracle_sequence for several sequences in a process pool."""
+    seqs = list(seqs)
+    workers = workers or _workers(len(seqs))
+    if workers == 1:
+        return _run(None, w, seqs, with_mass, with_pools)
+    with _pool(workers) as ex:
+        return _run(ex, w, seqs, with_mass, with_pools)
+
+
+def oracle_chunks(w, seqs, size=16, with_mass=False, with_pools=True):
+    """oracle_sequence over consecutive chunks of `size` sequences, on one process
+    pool (a generator: each chunk's pools are dropped once the caller moves on)."""
+    seqs = list(seqs)
+    workers = _workers(size)
+    ex = _pool(workers) if workers > 1 else None
+    try:
+        for i in range(0, len(seqs), size):
+            yield _run(ex, w, seqs[i:i + size], with_mass, with_pools)
+    finally:
+        if ex is not None:
+            ex.shutdown()

@@ -19,9 +19,15 @@ pytestmark = pytest.mark.skipif(not os.path.exists(pa.LIB_PATH), reason="libpa.s
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "pa.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", src)))
+    """Every pa_* function that a header under include/ declares."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -34,8 +40,34 @@ def test_header_declares_the_entry_points():
 
 def test_library_exports_every_declared_function():
     L = pa.lib()
-    for n in _declared_functions():
+    names = _declared_functions()
+    assert "pa_probe_stream" in names and "pa_probe_gather" in names
+    for n in names:
         assert hasattr(L, n), n
+
+
+def test_probe_argument_errors():
+    """The read-ceiling probes refuse bad shapes before any launch."""
+    L = pa.lib()
+    vp = ctypes.c_void_p
+    E = -1   # PA_ERR_INVALID_ARG
+    assert L.pa_probe_stream(None, 1 << 20, 64, vp(FAKE), None) == E
+    assert L.pa_probe_stream(vp(FAKE + 4), 1 << 20, 64, vp(FAKE), None) == E     # misaligned
+    assert L.pa_probe_stream(vp(FAKE), 1 << 20, 62, vp(FAKE), None) == E         # waves % 4
+    assert L.pa_probe_stream(vp(FAKE), (1 << 20) + 512, 64, vp(FAKE), None) == E  # bytes % (1 KiB * waves)
+    ok = dict(pool=vp(FAKE), pool_bytes=1 << 24, ids=vp(FAKE), waves=64, ipw=16, bb=2048,
+              inf=2, sink=vp(FAKE))
+
+    def g(**kw):
+        a = dict(ok, **kw)
+        return L.pa_probe_gather(a["pool"], a["pool_bytes"], a["ids"], a["waves"], a["ipw"],
+                                 a["bb"], a["inf"], a["sink"], None)
+    assert g(bb=3000) == E
+    assert g(inf=3) == E
+    assert g(ipw=6, inf=4) == E
+    assert g(pool_bytes=1024) == E
+    assert g(ids=None) == E
+    assert g(waves=0) == E
 
 
 def _cache(**kw):

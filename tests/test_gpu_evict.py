@@ -58,7 +58,8 @@ def scored_case(w, seqs, partitions, steps=1, flagged=()):
     dw.step_append()
     for b in flagged:                      # stale expected tag: the request is aborted
         dw.expected_tags[b].view(-1)[0] ^= 1
-    ora = oracle_sequences_parallel(w, [b for b in seqs if b not in flagged], with_mass=True)
+    ora = oracle_sequences_parallel(w, [b for b in seqs if b not in flagged], with_mass=True,
+                                    with_pools=False)
     rng = np.random.default_rng(w.cfg_id)
     live = [b for b in seqs if b not in flagged]
     read = _read_slots(w, live)
@@ -122,8 +123,12 @@ def test_scored_fp8_other_formats(layout, D):
     scored_case(w, seqs=range(w.B), partitions=(0, 4))
 
 
-def test_scored_workload5_full_size_sampled():
-    scored_case(make_workload(5), seqs=[0, 41], partitions=(8,))
+@pytest.mark.timeout(900)
+def test_scored_workload5_full():
+    """The 70B-shaped FP8 workload, all 64 sequences: outputs bitwise those of
+    pa_decode, and every read score slot against the oracle's mass."""
+    w = make_workload(5)
+    scored_case(w, seqs=range(w.B), partitions=(8,))
 
 
 # ------------------------------------------------------------ compaction

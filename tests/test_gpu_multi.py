@@ -25,6 +25,7 @@ from tests.test_gpu_parity import (
     log,
     out_f64,
     run_case,
+    run_full_case,
 )
 
 pytestmark = pytest.mark.gpu
@@ -89,12 +90,14 @@ def test_multi_column_tiles(cfg, heads, T, kw):
     run_case(w, partitions=(0, 1, 8))
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [4, 8])
-def test_multi_workload5_full_size_sampled(T):
+def test_multi_workload5_full(T):
     """70B-shaped FP8 cache, L = 32768, T = 4 or 8 drafts (32 or 64 columns per
-    unit): the automatic split the benchmark times (split-K 4) and split-K 8."""
-    w = make_workload(5, q_len=T)
-    run_case(w, seqs=[0, 37, 63], partitions=(0, 8), pools=False, fill_seqs=None)
+    unit), all 64 sequences against the oracle: the automatic split the
+    benchmark times (split-K 4) and split-K 8; the pages of the T-token
+    append (re-quantised where the drafts raise a page's scale) bit for bit."""
+    run_full_case(make_workload(5, q_len=T), partitions=(0, 8), pools=(T == 8))
 
 
 def test_multi_lengths_shorter_than_the_drafts():

@@ -4,12 +4,12 @@ A negative scale reverses the ranking of the scores, zero makes the weights
 uniform over the attended tokens, and a large one makes them nearly one-hot.
 Each is checked against the fp64 oracle run with the same scale, for plain
 decode (fixed and balanced splits), 4 drafts and a short prefill chunk, BF16
-and FP8.  Bars: those of the other parity tests (max-abs 1e-2, mean-abs 1e-3)
-where the output averages many rows (|o| well below 1); with the sharp scale an
-output is close to one V row (|o| up to about 4), and the kernel's two BF16
-roundings -- the weights P as MFMA operands and the output -- allow up to
-u * (|o| + max|V|) with u = 2^-8, so that is the per-element bar there (mean-abs
-still 1e-3); max|V| < 6.5 for these N(0, 1) draws.
+and FP8.  Bars: mean-abs 1e-3 everywhere, and per element max-abs 1e-2
+against the fp64 oracle -- except where the output's own BF16 step is coarser
+than that bar: with the sharp scale an output is close to one V row (|o| up to
+about 4), and one BF16 ulp is 2^-6 for |o| in [2, 4) and 2^-5 in [4, 8), so
+even the correctly rounded oracle is up to half of that away from it.  There
+an element passes within one BF16 ulp of bf16_RNE(oracle).
 """
 import numpy as np
 import pytest
@@ -18,15 +18,19 @@ import torch
 from decode_attention_paged_pa_amd import pa
 from decode_attention_paged_pa_amd.device_inputs import build_device_workload
 from decode_attention_paged_pa_amd.workloads import make_workload
-from oracle import oracle_decode, oracle_decode_multi
+from oracle import bf16_from_f32_rne, bf16_to_f64, oracle_decode, oracle_decode_multi
 from tests.oracle_fill import oracle_fill
 from tests.test_gpu_parity import MAX_ABS, MEAN_ABS, log, out_f64
 
 pytestmark = pytest.mark.gpu
 
 SCALES = (-1.0, 0.0, 4.0)   # multiples of the workload's own 1/sqrt(D)
-U_BF16 = 2.0 ** -8
-V_MAX = 6.5
+
+
+def bf16_ulp(y):
+    """One BF16 ulp at the values y (BF16 values, fp64): 2^(floor(log2|y|) - 7)."""
+    a = np.abs(y)
+    return np.where(a > 0, 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7), 2.0 ** -133)
 
 
 def _check(got, ref, what, sharp):
@@ -34,10 +38,11 @@ def _check(got, ref, what, sharp):
     log("%s: max-abs %.3g mean-abs %.3g" % (what, e.max(), e.mean()))
     assert np.all(np.isfinite(got))
     assert e.mean() <= MEAN_ABS, e.mean()
-    if sharp:
-        excess = e - U_BF16 * (np.abs(ref) + V_MAX)
-        assert excess.max() <= 0, excess.max()
-    else:
+    rounded = bf16_to_f64(bf16_from_f32_rne(ref.astype(np.float32)))
+    ulp = bf16_ulp(rounded)
+    ok = (e <= MAX_ABS) | ((ulp > MAX_ABS) & (np.abs(got - rounded) <= ulp))
+    assert ok.all(), (e[~ok][:4], ref[~ok][:4])
+    if not sharp:
         assert e.max() <= MAX_ABS, e.max()
 
 
