@@ -29,11 +29,12 @@ def hipcc_flags():
     ]
 
 
-def build(verbose=False, extra_flags=(), out_path=None, src_dir=None):
+def build(verbose=False, extra_flags=(), out_path=None, src_dir=None, link_flags=()):
     """Compile every source and link libpa.so; raises on failure.
 
-    extra_flags (e.g. -D tuning knobs), out_path and src_dir serve parameter
-    sweeps and comparisons with other versions of the sources.
+    extra_flags (e.g. -D tuning knobs), link_flags, out_path and src_dir serve
+    parameter sweeps, instrumented host builds and comparisons with other
+    versions of the sources.
     """
     out_path = out_path or LIB_PATH
     src_dir = src_dir or CSRC
@@ -50,7 +51,7 @@ def build(verbose=False, extra_flags=(), out_path=None, src_dir=None):
         _run(cmd, verbose)
         objs.append(obj)
     tmp = out_path + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + list(link_flags) + objs
     _run(cmd, verbose)
     os.replace(tmp, out_path)
     return out_path

@@ -276,6 +276,11 @@ int append_args(const pa_cache_desc* cache, const pa_seq_desc* seq, const int32_
   a.n_new = n_new;
   a.k_new = k_new;
   a.v_new = v_new;
+  if (seq->expected_tags) {   // writes gated on the tags of the pages they land in
+    if (!cache->page_tags || !aligned(cache->page_tags, 4)) return PA_ERR_INVALID_ARG;
+    a.expected_tags = seq->expected_tags;
+    a.page_tags = cache->page_tags;
+  }
   a.batch = seq->batch;
   a.num_kv_heads = cache->num_kv_heads;
   a.head_dim = cache->head_dim;

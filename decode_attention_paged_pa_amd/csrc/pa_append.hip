@@ -26,7 +26,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   append_item<D, FP8, 256>(a, blockIdx.x, true, threadIdx.x, s_red, s_old);
 }
 
-// One thread per sequence: range and length bits of this append.
+// One thread per sequence: range and length bits of this append, and with
+// expected tags, bit 0 for a page it would write whose tag is not the
+// expected one (that page is left alone).
 __global__ __launch_bounds__(256) void append_flags_kernel(AppendArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.batch) return;
@@ -43,7 +45,13 @@ __global__ __launch_bounds__(256) void append_flags_kernel(AppendArgs a) {
     const int hi = min(lo + n, cap);
     const int32_t* bt = a.block_table + (size_t)row * a.table_width;
     for (int i = lo / kPageSize; i * kPageSize < hi; ++i) {
-      if ((unsigned)bt[i] >= (unsigned)a.num_pages) bits |= 2u;
+      const int p = bt[i];
+      if ((unsigned)p >= (unsigned)a.num_pages) {
+        bits |= 2u;
+      } else if (a.expected_tags &&
+                 a.expected_tags[(size_t)row * a.table_width + i] != a.page_tags[p]) {
+        bits |= 1u;
+      }
     }
   }
   a.flags[b] = bits;

@@ -63,6 +63,12 @@ __device__ __forceinline__ float bf16_value(uint16_t bits) { return __uint_as_fl
 // over everything written since the page started.  The new tokens' amax may
 // raise it, and then the page's earlier codes are re-quantised.
 //
+// A page is written only through a table entry whose expected tag (when the
+// request gives them) is the page's current tag: the integrity check of
+// "Cloudflare quantizes Kimi and GLM caches for 41% faster inference"
+// (integrity-check paragraph) protects requests that share GPU memory, and a
+// stale entry names a page that may now hold another request's tokens.
+//
 // Every thread passes the FP8 path's one barrier exactly once, whether or not
 // its item writes anything (inactive items, items past the unit's last page,
 // unwritable pages), so items of different units may share a workgroup.
@@ -88,8 +94,10 @@ __device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
       const int pos_lo = max(lo, i * kPageSize);
       const int pos_hi = min(min(lo + n, (i + 1) * kPageSize), cap);
       if (pos_lo < pos_hi) {
-        const int p = a.block_table[(size_t)row * a.table_width + i];
-        if ((unsigned)p < (unsigned)a.num_pages) {
+        const size_t e = (size_t)row * a.table_width + i;
+        const int p = a.block_table[e];
+        if ((unsigned)p < (unsigned)a.num_pages &&
+            (a.expected_tags == nullptr || a.expected_tags[e] == a.page_tags[p])) {
           pid = p;
           slot0 = pos_lo - i * kPageSize;
           cnt = pos_hi - pos_lo;

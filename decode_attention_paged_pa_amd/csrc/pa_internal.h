@@ -77,6 +77,11 @@ struct AppendArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   uint32_t* flags;
+  // With expected_tags (the table's shape) a page is written only while its
+  // tag is the one the request expects: a stale entry may name a page that
+  // now belongs to another request.
+  const uint32_t* expected_tags;
+  const uint32_t* page_tags;
   int batch, num_kv_heads, head_dim, table_width, num_pages, n_max;
   int pages_per_unit;         // ceil(n_max / S) + 1: grid slots per unit
   bool head_layout, fp8;

@@ -30,9 +30,11 @@ class DeviceWorkload:
     expected_tags: torch.Tensor
     flags: torch.Tensor         # [B] int32 (uint32 bit patterns)
 
-    def step_append(self, flags=None):
+    def step_append(self, flags=None, check=True):
+        """The step's append; with check, through the expected tags (a page whose tag
+        is stale is left alone), as pa_decode_step does it."""
         pa.append(self.cache, self.block_table, self.lens_old, self.n_step, self.k_step,
-                  self.v_step, flags=flags)
+                  self.v_step, flags=flags, expected_tags=self.expected_tags if check else None)
 
     def decode_step(self, check=True, num_partitions=0, out=None, workspace=None, events=None):
         """The step's append and decode (T <= 8) in one library call."""

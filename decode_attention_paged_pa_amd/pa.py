@@ -20,7 +20,10 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
+# PA_LIB_PATH points the binding at another build of the library (an
+# instrumented host build in the tests); by default, the in-tree libpa.so.
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
 
 LAYOUT = {"seq": 0, "head": 1}
 KV_DTYPE = {"bf16": 0, "fp8": 1}
@@ -230,9 +233,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def append(cache, block_table, lens, n_new, k_new, v_new, flags=None, stream=None):
-    """pa_cache_append: write n_new[u] tokens of k_new/v_new [B][Hkv][n_max][D] (BF16)."""
-    sd = _seq(cache, block_table, lens)
+def append(cache, block_table, lens, n_new, k_new, v_new, flags=None, stream=None,
+           expected_tags=None):
+    """pa_cache_append: write n_new[u] tokens of k_new/v_new [B][Hkv][n_max][D] (BF16);
+    with expected_tags, only into pages whose tag is the expected one."""
+    sd = _seq(cache, block_table, lens, expected_tags)
     _need(n_new, "n_new", I32)
     if tuple(n_new.shape) != tuple(lens.shape):
         raise ValueError("n_new must have the shape of lens")

@@ -147,8 +147,12 @@ size_t pa_pool_bytes(const pa_cache_desc *cache);
  *   n_new:  device int32, SEQ [B], HEAD [B][Hkv]; 0 <= n_new <= n_max.
  *   k_new, v_new: device BF16 [B][Hkv][n_max][D].
  *   seq->lens are the lengths BEFORE the append; the library never updates
- *   lengths or the table.  seq->expected_tags is ignored (tags are checked
- *   before reads only).
+ *   lengths or the table.
+ *   seq->expected_tags (NULL or the table's shape; then cache->page_tags is
+ *   required): a page is written only through a table entry whose expected
+ *   tag equals the page's tag ([tags]: a stale entry may name a page that was
+ *   reallocated to another request, whose tokens must not be overwritten).
+ *   Tokens of a page that fails this test are not written.
  * BF16 caches get a copy of the bits.  FP8 caches, per (page, head) and
  * separately for K and V: s = fl32(amax / 448) over every value written since
  * the page was last started at slot 0 (a write starting at slot 0 resets the
@@ -157,7 +161,8 @@ size_t pa_pool_bytes(const pa_cache_desc *cache);
  * RNE_e4m3(saturate(fl32(fl32(decode(c) * s_old) / s_new))).
  * Tokens whose page id is out of range, or beyond table_width * S, are not
  * written.  flags (device uint32 [B], may be NULL) is overwritten with
- * PA_FLAG_PAGE_OOB / PA_FLAG_LEN_OVERFLOW bits of this call.
+ * PA_FLAG_PAGE_OOB / PA_FLAG_LEN_OVERFLOW bits of this call, and with
+ * PA_FLAG_TAG_MISMATCH for a page left alone because of its tag.
  * Pages must not be shared by two units within one call.
  */
 int pa_cache_append(const pa_cache_desc *cache, const pa_seq_desc *seq, const int32_t *n_new,
@@ -275,7 +280,10 @@ int pa_decode_multi_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
  *   n_new, n_max, k_new, v_new: as pa_cache_append.
  *   everything else: as pa_decode / pa_decode_multi, including the workspace
  *   (their *_workspace_bytes) and the flags, which are the decode's
- *   validation of seq (the append itself sets no flag bits).
+ *   validation of seq (the append itself sets no flag bits).  With
+ *   seq->expected_tags the append writes only pages whose tag is the expected
+ *   one, as pa_cache_append does; such a mismatch is also a mismatch of an
+ *   entry the decode reads, so the sequence is flagged.
  * Pages, scales and outputs are bit-identical to the two calls made one after
  * the other.  The append shares the validation's launch (three launches
  * instead of four); errors as the two calls, checked before any launch.

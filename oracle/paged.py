@@ -34,8 +34,13 @@ Readings taken where the pages are silent (each is also in the design notes):
      from s_old to s_new, the codes already in the page are re-quantised as
      e4m3_rne_sat(fl32(fl32(dec(c) * s_old) / s_new)).  A page whose first
      written slot in a call is slot 0 is fresh: its old scale is ignored.
-  R5 Append never checks tags; it still refuses out-of-range page ids (flag
-     bit 1) and writes past table_width * S (flag bit 2).
+  R5 Append refuses out-of-range page ids (flag bit 1) and writes past
+     table_width * S (flag bit 2).  Given the tags a request expects, it
+     writes a page only through an entry whose expected tag is the page's
+     current tag, and otherwise leaves the page alone and sets flag bit 0:
+     the check exists to protect requests that share GPU memory, and a
+     stale entry names a page that may now hold another request's tokens
+     (integrity-check paragraph).  Without expected tags it checks none.
   R6 Validation flags, per sequence b, OR-ed over its units: bit 0 a tag
      mismatch, bit 1 a page id outside [0, P) (its tag is then not compared),
      bit 2 a length above table_width * S (entries checked up to the width).
@@ -157,12 +162,14 @@ def _append_fp8_page(pool, scales, pid, ph, first_slot, slots, new_bits):
     scales[pid, ph] = s_new
 
 
-def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width):
+def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width,
+                  expected_tags=None, page_tags=None):
     """Write n_new[u] tokens per unit at positions lens_old[u] ... .
 
     block_table: int32 [B][W] (SEQ) or [B][Hkv][W] (HEAD)
     lens_old, n_new: int32 [B] (SEQ) or [B][Hkv] (HEAD)
     k_new, v_new: bf16 bits uint16 [B][Hkv][n_max][D]
+    expected_tags (the table's shape) with page_tags (uint32 [P]): R5's gate.
     Updates `cache` in place and returns the per-sequence flags (uint32 [B]).
     """
     c = cache
@@ -183,6 +190,10 @@ def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width
             pid = int(table[i])
             if not (0 <= pid < P):
                 flags[b] |= FLAG_PAGE_OOB
+                t += cnt
+                continue
+            if expected_tags is not None and expected_tags[row][i] != page_tags[pid]:
+                flags[b] |= FLAG_TAG_MISMATCH        # the page is someone else's now
                 t += cnt
                 continue
             slots = np.arange(slot0, slot0 + cnt)

@@ -19,9 +19,12 @@ def seq_rows(w, b):
     return bt, w.lens[b:b + 1]
 
 
-def oracle_fill(w, seqs=None, cache=None):
+def oracle_fill(w, seqs=None, cache=None, step_tags=True):
     """Replay the appends of sequences `seqs` (default: all) into an oracle cache.
 
+    The bulk fill writes the history into fresh pages; the step's append goes
+    through the expected tags (with step_tags), as the GPU step does: a page
+    whose entry is stale is left alone.
     Returns (cache, kv) where kv[b] = the generator's draws for sequence b.
     """
     if cache is None:
@@ -43,8 +46,10 @@ def oracle_fill(w, seqs=None, cache=None):
             n1 = n_hist[None, :].astype(np.int32)
             one = np.where(w.lens[b:b + 1] > 0, w.q_len, 0).astype(np.int32)
         f1 = oracle_append(cache, bt, zero, n1, k_hist[None], v_hist[None], w.W)
-        f2 = oracle_append(cache, bt, n1, one, k_new[None], v_new[None], w.W)
-        assert f1[0] == 0 and f2[0] == 0
+        tags = dict(expected_tags=w.expected_tags[b:b + 1], page_tags=w.page_tags) \
+            if step_tags else {}
+        f2 = oracle_append(cache, bt, n1, one, k_new[None], v_new[None], w.W, **tags)
+        assert f1[0] == 0 and (f2[0] & ~np.uint32(1)) == 0
     return cache, kv
 
 
@@ -111,6 +116,17 @@ class _SubWorkload:
         self.block_table = local_table
         self.lens = w.lens[b:b + 1]
         self.q_len = w.q_len
+        # the local pages carry their global pages' tags; entries keep theirs
+        self.expected_tags = np.zeros(local_table.shape, np.uint32)
+        self.page_tags = np.zeros(n_pages, np.uint32)
+        if w.page_tags is not None:
+            rows = w.block_table[b:b + 1].reshape(-1, w.W)
+            loc = local_table.reshape(-1, w.W)
+            exp = w.expected_tags[b:b + 1].reshape(-1, w.W)
+            for r in range(rows.shape[0]):
+                used = loc[r] != 0x7FFFFFFF
+                self.expected_tags.reshape(-1, w.W)[r, used] = exp[r, used]
+                self.page_tags[loc[r, used]] = w.page_tags[rows[r, used]]
 
     def seq_kv(self, _):
         return self._w.seq_kv(self._b)

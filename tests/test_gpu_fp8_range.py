@@ -12,10 +12,13 @@ head against bars in the units of that head's values (m = max |V| over the
 unit's tokens): the kernel's P.V operand carries an f16 relative error of at
 most 2^-11 per weight, and the weights sum to 1, so the P rounding moves an
 output by at most 2^-11 m; the BF16 output rounding adds at most 2^-9 |o| <=
-2^-9 m.  The bars are max |err| <= 2^-8 m and mean |err| <= 2^-12 m (for
-N(0, 1) values, m is about 4.5 and these are 1.8e-2 and 1.1e-3: the usual
-1e-2 / 1e-3 bars in that head's units).  Where K and V are scaled by one
-constant f, the usual bars times f apply as well.
+2^-9 m.  The bars are max |err| <= 2^-8 m and mean |err| <= 2^-12 m +
+2^-9 mean |o|: for N(0, 1) values averaged over many tokens, m is about 4.5
+and |o| well below 1, so these are about 1.8e-2 and 1.1e-3, the usual 1e-2 /
+1e-3 bars in that head's units; the second mean term is the output's own
+rounding, which is all the error there is where a unit holds one token (the
+output is then one V row).  Where K and V are scaled by one constant f, the
+usual bars times f apply as well.
 """
 import numpy as np
 import pytest
@@ -59,7 +62,8 @@ def check_rows(w, out, ora, seqs, flags, const=None, what=""):
             e = err[:, h * w.G:(h + 1) * w.G, :]
             m = vmax[h]
             assert e.max() <= MAX_REL * m, (what, b, h, e.max(), m)
-            assert e.mean() <= MEAN_REL * m, (what, b, h, e.mean(), m)
+            o_mean = np.abs(r).reshape(-1, w.Hq, w.D)[:, h * w.G:(h + 1) * w.G, :].mean()
+            assert e.mean() <= MEAN_REL * m + 2.0 ** -9 * o_mean, (what, b, h, e.mean(), m)
             worst = max(worst, e.max() / m if m else 0.0)
             if const is not None:
                 assert e.max() <= 1e-2 * const and e.mean() <= 1e-3 * const, (what, b, h)

@@ -1,7 +1,8 @@
 """pa_decode_step (a decode step's append and decode in one call) on the GPU.
 
 The step's append runs in the same launch as the decode's validation and split
-plan.  Its pages, scales, outputs and flags must be those of pa_cache_append
+plan, and writes only pages whose tag is the expected one.  Its pages, scales,
+outputs and flags must be those of pa_cache_append (with the expected tags)
 followed by pa_decode / pa_decode_multi, bit for bit; the outputs are also
 checked against the fp64 oracle with the bars of the other parity tests
 (max-abs 1e-2, mean-abs 1e-3, flags bit-exact, flagged rows +0.0).
@@ -12,6 +13,7 @@ import torch
 
 from decode_attention_paged_pa_amd import pa
 from decode_attention_paged_pa_amd.device_inputs import build_device_workload
+from decode_attention_paged_pa_amd.layout import v_block_slots
 from decode_attention_paged_pa_amd.workloads import make_workload
 from tests.oracle_fill import oracle_sequences_parallel
 from tests.test_gpu_parity import compare_outputs, compare_pools, expected_flags, flags_of, log
@@ -118,3 +120,62 @@ def test_step_full_size_matches_append_then_decode():
     assert torch.equal(dw.flags, ref_flags)
     for got, want in zip(_state(dw.cache), ref_state):
         assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("kv,layout", [("fp8", "seq"), ("bf16", "seq"), ("fp8", "head")])
+def test_step_append_through_a_stale_entry_leaves_the_page_alone(kv, layout):
+    """Sequence 1's step token lands in table entry i, which is stale: it names
+    page X, now a full page of sequence 0 (whose tag moved on).  The step must
+    leave X's bytes and scales alone, flag sequence 1 only, and give sequence 0
+    its oracle output; pa_cache_append with the expected tags does the same and
+    flags the page (the integrity-check paragraph: the check protects requests
+    that share GPU memory)."""
+    if layout == "head":
+        lens = np.array([[700, 300, 33, 900, 64, 17, 450, 1000], [500, 81, 600, 20, 90, 700, 3, 40]])
+    else:
+        lens = [700, 501]
+    w = make_workload(3, lens=lens, kv=kv, layout=layout, stale_frac=0.0)
+    dw = build_device_workload(w)
+    row1 = (1,) if layout == "seq" else (1, 0)
+    row0 = (0,) if layout == "seq" else (0, 0)
+    L1 = int(w.lens[row1])
+    i = (L1 - 1) // 16                                 # the entry holding sequence 1's step token
+    X = int(w.block_table[row0][5])                    # a full page of sequence 0
+    bt = w.block_table.copy()
+    exp = w.expected_tags.copy()
+    bt[row1][i] = X
+    exp[row1][i] = np.uint32((int(w.page_tags[X]) - 1) % 2 ** 32)
+    dw.block_table.copy_(torch.from_numpy(bt).cuda())
+    dw.expected_tags.copy_(torch.from_numpy(exp.view(np.int32)).cuda())
+    before = _state(dw.cache)
+    out = dw.decode_step(check=True)
+    torch.cuda.synchronize()
+    assert flags_of(dw).tolist() == [0, 1]
+    after = _state(dw.cache)
+    kp_b, kp_a = before[0].view(w.P, -1), after[0].view(w.P, -1)
+    changed = set((kp_a != kp_b).any(dim=1).nonzero().flatten().tolist())
+    rows0 = [w.block_table[0]] if layout == "seq" else list(w.block_table[0])
+    lens0 = [int(w.lens[0])] if layout == "seq" else list(w.lens[0])
+    step0 = {int(r[(L - 1) // 16]) for r, L in zip(rows0, lens0)}
+    assert changed <= step0, (changed, step0)         # only sequence 0's step pages moved
+    assert X not in changed
+    sp, sh = v_block_slots(w.layout, w.P, w.Hkv)      # X's V blocks sit in other slots
+    H = w.Hkv if layout == "seq" else 1
+    vp_b, vp_a = before[1].view(w.P, H, -1), after[1].view(w.P, H, -1)
+    for h in range(H):
+        assert torch.equal(vp_a[sp[X, h], sh[X, h]], vp_b[sp[X, h], sh[X, h]])
+    if kv == "fp8":
+        for j in (2, 3):
+            assert torch.equal(after[j].view(w.P, -1)[X], before[j].view(w.P, -1)[X])
+    w2 = make_workload(3, lens=lens, kv=kv, layout=layout, stale_frac=0.0)
+    w2.block_table, w2.expected_tags = bt, exp
+    ora = oracle_sequences_parallel(w2, [0])
+    compare_outputs(out, ora, [0, 1], flags_of(dw), "stale entry")
+    # the same through pa_cache_append: the page is left alone and flagged
+    _restore(dw.cache, before)
+    fl = torch.full((w.B,), -1, dtype=torch.int32, device="cuda")
+    pa.append(dw.cache, dw.block_table, dw.lens_old, dw.n_step, dw.k_step, dw.v_step, flags=fl,
+              expected_tags=dw.expected_tags)
+    torch.cuda.synchronize()
+    assert fl.cpu().numpy().view(np.uint32).tolist() == [0, 1]
+    assert torch.equal(_state(dw.cache)[0].view(w.P, -1)[X], kp_b[X])

@@ -160,3 +160,63 @@ def test_p9_unread_entries_are_not_checked():
     bt[0, 2] = -5
     fl = oracle_validate(w.layout, w.P, w.S, bt, w.lens, w.page_tags, exp, w.W)
     assert fl.tolist() == [0, 0]
+
+
+def _gated_case(kv):
+    """Two SEQ sequences; sequence 1's entry 2 is stale and names page 5, which
+    belongs to sequence 0 now (sequence 0 writes into it in the same call)."""
+    S, D, W, P = 16, 4, 4, 12
+    bt = np.array([[4, 5, 9, 10], [0, 1, 5, 11]], np.int32)
+    tags = np.arange(100, 100 + P, dtype=np.uint32)
+    exp = tags[np.clip(bt, 0, P - 1)].astype(np.uint32)
+    exp[1, 2] = tags[5] - 1                       # the tag page 5 had before reallocation
+    lens_old = np.array([20, 30], np.int32)       # seq 0 writes pages 5 and 9; seq 1 pages 1 and 5
+    n_new = np.array([14, 5], np.int32)
+    rng = np.random.default_rng(3)
+    k = to_bf16_bits(rng.standard_normal((2, 1, 14, D)).astype(np.float32))
+    v = to_bf16_bits(rng.standard_normal((2, 1, 14, D)).astype(np.float32))
+    cache = OracleCache("seq", kv, P, S, 1, D)
+    fl = oracle_append(cache, bt, lens_old, n_new, k, v, W, expected_tags=exp, page_tags=tags)
+    return cache, fl, bt, exp, tags, lens_old, n_new, k, v
+
+
+def test_p10_append_skips_pages_whose_tag_is_stale():
+    """R5's gate: sequence 1's two tokens for page 5 (through its stale entry) are
+    not written and flag bit 0; everything else is written; brute force over
+    every token with the rule written as a predicate."""
+    cache, fl, bt, exp, tags, lens_old, n_new, k, v = _gated_case("bf16")
+    assert fl.tolist() == [0, FLAG_TAG_MISMATCH]
+    want_k = np.full(cache.k.shape, 0x7FC0, np.uint16)
+    for b in range(2):
+        for t in range(int(n_new[b])):
+            pos = int(lens_old[b]) + t
+            i, slot = pos // 16, pos % 16
+            pid = int(bt[b, i])
+            if exp[b, i] == tags[pid]:
+                want_k[pid, 0, slot] = k[b, 0, t]
+    assert np.array_equal(cache.k, want_k)
+    assert np.all(cache.k[5, 0, :4] == 0x7FC0)                 # seq 0 starts page 5 at slot 4
+    assert np.array_equal(cache.k[5, 0, 4:16], k[0, 0, :12])   # seq 0's tokens, not seq 1's
+
+
+def test_p10_fp8_page_behind_a_stale_entry_keeps_codes_and_scale():
+    cache, fl, bt, exp, tags, lens_old, n_new, k, v = _gated_case("fp8")
+    assert fl.tolist() == [0, FLAG_TAG_MISMATCH]
+    # pages 5 and 9 are exactly what sequence 0's append alone makes of them
+    only0 = OracleCache("seq", "fp8", 12, 16, 1, 4)
+    oracle_append(only0, bt, lens_old, np.array([14, 0], np.int32), k, v, 4,
+                  expected_tags=exp, page_tags=tags)
+    for p in (5, 9):
+        assert np.array_equal(cache.k[p], only0.k[p]) and np.array_equal(cache.v[p], only0.v[p])
+        assert cache.k_scale[p, 0].tobytes() == only0.k_scale[p, 0].tobytes()
+        assert cache.v_scale[p, 0].tobytes() == only0.v_scale[p, 0].tobytes()
+
+
+def test_p10_no_expected_tags_no_gate():
+    """Without expected tags the append checks none (sequence 1 overwrites slots
+    of page 5: the hazard the gate removes)."""
+    _, _, bt, exp, tags, lens_old, n_new, k, v = _gated_case("bf16")
+    cache = OracleCache("seq", "bf16", 12, 16, 1, 4)
+    fl = oracle_append(cache, bt, lens_old, n_new, k, v, 4)
+    assert fl.tolist() == [0, 0]
+    assert np.array_equal(cache.k[5, 0, 0:3], k[1, 0, 2:5])    # positions 32..34 of seq 1
