@@ -48,7 +48,37 @@ def v_block_slots(layout, num_pages, num_kv_heads):
 
 
 def pool_to_logical(pool_bytes, which, layout, kv_dtype, num_pages, num_kv_heads, head_dim):
-    """Raw pool bytes (numpy uint8, flat) -> [P][H][S][D] (H = Hkv, or 1 for HEAD)."""
+    """Raw pool bytes (numpy uint8, flat) -> [P][H][S][D] (H = Hkv, or 1 for HEAD).
+
+    Both block orders are axis permutations of a block: K is [D / 4CE][S][4CE]
+    and V is [D / (16 TPC)][16][S / 4][TPC][4] (dims c, then token groups;
+    d = 16 (TPC jh + jl) + c, t = 4 tq + tr), so a reshape and a transpose
+    read them back; the V blocks are first moved from their slots
+    (v_block_slots).  Equal to indexing with k_offsets / v_offsets."""
+    esize = 1 if kv_dtype == "fp8" else 2
+    dt = np.uint8 if esize == 1 else np.uint16
+    H = num_kv_heads if layout == "seq" else 1
+    D = head_dim
+    blocks = np.asarray(pool_bytes).view(dt).reshape(num_pages, H, S * D)
+    if which == "k":
+        seg = 64 // esize
+        return np.ascontiguousarray(
+            blocks.reshape(num_pages, H, D // seg, S, seg).transpose(0, 1, 3, 2, 4)
+        ).reshape(num_pages, H, S, D)
+    if layout == "seq" and num_kv_heads > 1:
+        slotted = np.roll(blocks, -1, axis=1)          # head h's V sits in head h + 1's slot
+    else:
+        sp, _ = v_block_slots(layout, num_pages, num_kv_heads)
+        slotted = blocks[sp[:, 0]]                     # page p's V sits in page p ^ 1's slot
+    tpc = 4 // esize
+    v = slotted.reshape(num_pages, H, D // 16 // tpc, 16, S // 4, tpc, 4)
+    # axes (p, h, jh, c, tq, jl, tr) -> (p, h, tq, tr, jh, jl, c)
+    return np.ascontiguousarray(v.transpose(0, 1, 4, 6, 2, 5, 3)).reshape(num_pages, H, S, D)
+
+
+def pool_to_logical_by_index(pool_bytes, which, layout, kv_dtype, num_pages, num_kv_heads,
+                             head_dim):
+    """pool_to_logical written with the element index maps (slow; checks the fast one)."""
     esize = 1 if kv_dtype == "fp8" else 2
     dt = np.uint8 if esize == 1 else np.uint16
     H = num_kv_heads if layout == "seq" else 1

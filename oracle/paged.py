@@ -162,6 +162,45 @@ def _append_fp8_page(pool, scales, pid, ph, first_slot, slots, new_bits):
     scales[pid, ph] = s_new
 
 
+def _append_whole_pages(c, table, i, whole, row, b, h, ph, t, k_new, v_new, flags,
+                        expected_tags, page_tags):
+    """R2-R5 for `whole` whole pages (table entries i ...), each started afresh
+    at slot 0 by this call: per page, s = fl32(amax / 448) and codes
+    e4m3_rne_sat(fl32(x / s)) (no earlier codes to re-quantise), the same
+    arithmetic as _append_fp8_page, done for all the pages at once.  Returns
+    the tokens handled, or 0 (the caller then goes page by page) when two
+    entries of the run name the same page."""
+    S, P = c.S, c.P
+    pids = np.asarray(table[i:i + whole], dtype=np.int64)
+    ok = (pids >= 0) & (pids < P)
+    if not ok.all():
+        flags[b] |= FLAG_PAGE_OOB
+    if expected_tags is not None:
+        exp = np.asarray(expected_tags[row][i:i + whole])
+        tag_ok = ok.copy()
+        tag_ok[ok] = exp[ok] == page_tags[pids[ok]]
+        if (ok & ~tag_ok).any():
+            flags[b] |= FLAG_TAG_MISMATCH
+        ok = tag_ok
+    sel = pids[ok]
+    if len(np.unique(sel)) != len(sel):
+        return 0
+    for pool, scales, src in ((c.k, c.k_scale, k_new), (c.v, c.v_scale, v_new)):
+        bits = src[b, h, t:t + whole * S].reshape(whole, S, -1)[ok]
+        if c.kv_dtype == "bf16":
+            pool[sel, ph] = bits
+            continue
+        x = bf16_to_f64(bits).astype(np.float32)                       # exact
+        amax = np.max(np.abs(x), axis=(1, 2)).astype(np.float32)
+        scale = (amax / E4M3_MAX_F32).astype(np.float32)              # fl32(amax / 448)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = (x / scale[:, None, None]).astype(np.float32)           # fl32(x / s)
+        codes = e4m3_from_f32_rne_sat(q)
+        pool[sel, ph] = np.where(scale[:, None, None] == 0, np.uint8(0), codes)
+        scales[sel, ph] = scale
+    return whole * S
+
+
 def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width,
                   expected_tags=None, page_tags=None):
     """Write n_new[u] tokens per unit at positions lens_old[u] ... .
@@ -186,6 +225,13 @@ def oracle_append(cache, block_table, lens_old, n_new, k_new, v_new, table_width
         while t < n_ok:                       # one page at a time
             pos = pos0 + t
             i, slot0 = pos // S, pos % S
+            whole = (n_ok - t) // S if slot0 == 0 else 0
+            if whole >= 2:                    # a run of whole fresh pages, all at once
+                done = _append_whole_pages(c, table, i, whole, row, b, h, ph, t, k_new, v_new,
+                                           flags, expected_tags, page_tags)
+                if done:
+                    t += done
+                    continue
             cnt = min(S - slot0, n_ok - t)
             pid = int(table[i])
             if not (0 <= pid < P):

@@ -138,12 +138,35 @@ def _workers(n):
     return max(1, min(16, len(os.sched_getaffinity(0)), n))
 
 
+_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
 def _pool(workers):
+    """A spawn pool whose workers run one BLAS/OpenMP thread each (one worker per
+    core; threaded BLAS in every worker would oversubscribe the cores).  The
+    workers start with the pool, under the environment set here."""
     import multiprocessing
+    import os
     from concurrent.futures import ProcessPoolExecutor
 
-    # spawn: a forked child of a process with live OpenMP/torch thread pools can deadlock
-    return ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn"))
+    saved = {k: os.environ.get(k) for k in _THREAD_VARS}
+    for k in _THREAD_VARS:
+        os.environ[k] = "1"
+    try:
+        # spawn: a forked child of a process with live OpenMP/torch thread pools can deadlock
+        ex = ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn"))
+        list(ex.map(_ready, range(workers)))   # start every worker now, under this environment
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return ex
+
+
+def _ready(_):
+    return True
 
 
 def _run(ex, w, seqs, with_mass, with_pools):

@@ -123,14 +123,6 @@ def test_scored_fp8_other_formats(layout, D):
     scored_case(w, seqs=range(w.B), partitions=(0, 4))
 
 
-@pytest.mark.timeout(900)
-def test_scored_workload5_full():
-    """The 70B-shaped FP8 workload, all 64 sequences: outputs bitwise those of
-    pa_decode, and every read score slot against the oracle's mass."""
-    w = make_workload(5)
-    scored_case(w, seqs=range(w.B), partitions=(8,))
-
-
 # ------------------------------------------------------------ compaction
 def _keep_lists(w, rng, frac, reverse_unit=None):
     """Keep lists per unit ([B][Hkv][K] and the lens-shaped counts).  SEQ: one count

@@ -219,15 +219,6 @@ def test_workload4_headwise_full():
 
 
 @pytest.mark.timeout(900)
-def test_workload5_full():
-    """The 70B-shaped FP8 layer at full size (64 x 32K tokens), in the launch
-    configuration the benchmark times (split-K 8) and the automatic split:
-    all 64 sequences against the oracle -- every pool byte and FP8 scale of
-    their 131,072 pages, the flags, and all 4,096 output rows."""
-    run_full_case(make_workload(5), partitions=(8, 0))
-
-
-@pytest.mark.timeout(900)
 def test_bf16_pools_beyond_4gib_sampled():
     """The 70B shape with a BF16 cache: each pool is 4.3 GB, so page offsets pass
     2^32 bytes (64-bit address arithmetic in append, validation and decode).  Two

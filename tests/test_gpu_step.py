@@ -99,29 +99,6 @@ def test_step_without_new_tokens_is_the_decode():
         assert torch.equal(got, want)
 
 
-def test_step_full_size_matches_append_then_decode():
-    """The 70B-shaped FP8 layer at full size (64 x 32K tokens, split-K 8, tag check
-    on), the benchmark's step: pa_decode_step against the two calls, bit for bit
-    (pools, scales, outputs, flags); the two calls are checked against the oracle
-    at this size in test_gpu_parity.py."""
-    w = make_workload(5)
-    dw = build_device_workload(w, log=log)
-    before = _state(dw.cache)
-    dw.step_append()
-    ref = dw.decode(check=True, num_partitions=8).clone()
-    torch.cuda.synchronize()
-    ref_flags = dw.flags.clone()
-    ref_state = _state(dw.cache)
-    _restore(dw.cache, before)
-    del before
-    out = dw.decode_step(check=True, num_partitions=8)
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
-    assert torch.equal(dw.flags, ref_flags)
-    for got, want in zip(_state(dw.cache), ref_state):
-        assert torch.equal(got, want)
-
-
 @pytest.mark.parametrize("kv,layout", [("fp8", "seq"), ("bf16", "seq"), ("fp8", "head")])
 def test_step_append_through_a_stale_entry_leaves_the_page_alone(kv, layout):
     """Sequence 1's step token lands in table entry i, which is stale: it names

@@ -412,3 +412,55 @@ def test_random_append_sequences_bit_exact(seed):
         for sl, cs in enumerate(codes):
             if cs is not None:
                 assert [int(c) for c in cache.k[pid, 0, sl]] == cs, (pid, sl)
+
+
+@pytest.mark.parametrize("layout", ["seq", "head"])
+def test_bulk_whole_pages_bit_exact_and_equal_to_page_by_page(layout):
+    """A bulk append from empty (runs of whole pages, done all at once by the
+    oracle) equals the exact rebuild, and equals the same tokens appended one
+    page at a time; an out-of-range id and a stale entry inside the run are
+    skipped and flagged the same way."""
+    rng = np.random.default_rng(21)
+    Hkv, D, W, P = 2, 8, 7, 40
+    n = 5 * S + 9
+    if layout == "seq":
+        bt = rng.permutation(P)[:W].astype(np.int32)[None]
+        lshape, tshape = (1,), (1, W)
+    else:
+        bt = rng.permutation(P)[:2 * W].astype(np.int32).reshape(1, Hkv, W)
+        lshape, tshape = (1, Hkv), (1, Hkv, W)
+    tags = rng.integers(0, 2 ** 32, size=P, dtype=np.uint64).astype(np.uint32)
+    exp = tags[bt].astype(np.uint32)
+    flat_bt, flat_exp = bt.reshape(-1, W), exp.reshape(-1, W)
+    flat_bt[0, 2] = P + 3                         # out of range, inside the run
+    flat_exp[-1, 1] ^= 1                          # stale, inside the run (last row)
+    mags = np.exp(rng.uniform(-3, 3, size=(1, Hkv, n, 1)))
+    x = (rng.standard_normal((1, Hkv, n, D)) * mags).astype(np.float32)
+    bits = to_bf16_bits(x)
+    zero, cnt = np.zeros(lshape, np.int32), np.full(lshape, n, np.int32)
+    bulk = OracleCache(layout, "fp8", P, S, Hkv, D)
+    fl = oracle_append(bulk, bt, zero, cnt, bits, bits, W, expected_tags=exp, page_tags=tags)
+    paged_ = OracleCache(layout, "fp8", P, S, Hkv, D)
+    fl2 = np.zeros(1, np.uint32)
+    for start in range(0, n, S):                  # the same tokens, one page per call
+        m = min(S, n - start)
+        fl2 |= oracle_append(paged_, bt, np.full(lshape, start, np.int32),
+                             np.full(lshape, m, np.int32), bits[:, :, start:start + m],
+                             bits[:, :, start:start + m], W, expected_tags=exp, page_tags=tags)
+    assert fl.tolist() == fl2.tolist() == [3]
+    assert np.array_equal(bulk.k, paged_.k) and np.array_equal(bulk.v, paged_.v)
+    assert bulk.k_scale.tobytes() == paged_.k_scale.tobytes()
+    # exact rebuild of every written page
+    for h in range(Hkv):
+        r = 0 if layout == "seq" else h
+        ph = h if layout == "seq" else 0
+        for i in range(-(-n // S)):
+            pid = int(flat_bt[r, i])
+            if not 0 <= pid < P or flat_exp[r, i] != tags[pid]:
+                continue
+            xs = bf16_to_f64(bits[0, h, i * S:(i + 1) * S])
+            s = exact_scale(np.max(np.abs(xs)))
+            assert Fraction(float(bulk.k_scale[pid, ph])) == s
+            for tt in range(xs.shape[0]):
+                for d in range(D):
+                    assert int(bulk.k[pid, ph, tt, d]) == exact_code(xs[tt, d], s)
