@@ -131,10 +131,11 @@ def test_step_append_through_a_stale_entry_leaves_the_page_alone(kv, layout):
     after = _state(dw.cache)
     kp_b, kp_a = before[0].view(w.P, -1), after[0].view(w.P, -1)
     changed = set((kp_a != kp_b).any(dim=1).nonzero().flatten().tolist())
-    rows0 = [w.block_table[0]] if layout == "seq" else list(w.block_table[0])
-    lens0 = [int(w.lens[0])] if layout == "seq" else list(w.lens[0])
-    step0 = {int(r[(L - 1) // 16]) for r, L in zip(rows0, lens0)}
-    assert changed <= step0, (changed, step0)         # only sequence 0's step pages moved
+    # the step pages of every unit but the stale one (HEAD: sequence 1's other
+    # heads append into their own pages)
+    units = [(0,), (1,)] if layout == "seq" else [(b, h) for b in range(2) for h in range(w.Hkv)]
+    steps = {int(w.block_table[u][(int(w.lens[u]) - 1) // 16]) for u in units if u != row1}
+    assert changed <= steps, (changed, steps)
     assert X not in changed
     sp, sh = v_block_slots(w.layout, w.P, w.Hkv)      # X's V blocks sit in other slots
     H = w.Hkv if layout == "seq" else 1
