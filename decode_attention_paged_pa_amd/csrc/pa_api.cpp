@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -475,6 +476,57 @@ PA_API int pa_decode(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t
                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr);
 }
 
+// ---------------------------------------------- pa_decode_noalloc's scratch
+// A static device array in place of the caller's workspace, for callers that
+// cannot allocate.  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address (one per GPU, each GPU holding its
+// own copy) comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in scratch_ptr[]; only that address is ever passed
+// to a kernel.
+namespace {
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kScratchDevices] = {};
+
+// The current device's scratch address; the stream must belong to that device.
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PA_ERR_LAUNCH;
+  if (dev >= kScratchDevices) return PA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess || sd != dev) return PA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
+}
+}  // namespace
+
+PA_API int pa_decode_noalloc(const pa_cache_desc* cache, const pa_seq_desc* seq,
+                             int32_t num_q_heads, const uint16_t* q, uint16_t* out,
+                             float softmax_scale, int32_t num_partitions, uint32_t* flags,
+                             pa_stream_t stream) {
+  const size_t need = pa_decode_workspace_bytes(cache, seq, num_q_heads, num_partitions);
+  if (need == (size_t)-1) {   // the argument errors, as pa_decode reports them
+    return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
+                       nullptr, 0, reinterpret_cast<hipStream_t>(stream), nullptr);
+  }
+  if (need > kScratchBytes) return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rc = device_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (rc != PA_OK) return rc;
+  return decode_impl(cache, seq, num_q_heads, 1, q, out, softmax_scale, num_partitions, flags,
+                     ws, kScratchBytes, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
 PA_API int pa_decode_timed(const pa_cache_desc* cache, const pa_seq_desc* seq,
                            int32_t num_q_heads, const uint16_t* q, uint16_t* out,
                            float softmax_scale, int32_t num_partitions, uint32_t* flags,
@@ -663,6 +715,9 @@ PA_API const char* pa_strerror(int code) {
              "group * q_len <= 64)";
     case PA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_SCRATCH:
+      return "the call needs more scratch than pa_decode_noalloc's static buffer holds "
+             "(PA_NOALLOC_SCRATCH_BYTES); use pa_decode with a workspace";
     default: return "unknown error code";
   }
 }

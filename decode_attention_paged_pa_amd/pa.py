@@ -124,6 +124,9 @@ def lib():
         L.pa_strerror.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
         L.pa_version.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = [P(CacheDesc), P(SeqDesc), i32, vp, vp, ctypes.c_float,
+                                        i32, vp, vp]
+        L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_probe_stream.argtypes = [vp, sz, i32, vp, vp]
         L.pa_probe_stream.restype = ctypes.c_int
         L.pa_probe_gather.argtypes = [vp, sz, vp, i32, i32, i32, i32, vp, vp]
@@ -287,6 +290,35 @@ def decode(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags
         raise ValueError("q must be [B][Hq][D]")
     return _decode(cache, q, 1, block_table, lens, softmax_scale, expected_tags, flags,
                    num_partitions, out, workspace, events, stream)
+
+
+def decode_noalloc(cache, q, block_table, lens, softmax_scale, expected_tags=None, flags=None,
+                   num_partitions=0, out=None, stream=None):
+    """pa_decode_noalloc: pa_decode with the library's static scratch in place of a
+    workspace (nothing allocated by the library; `out` must be given by callers
+    that cannot allocate either)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][D]")
+    sd = _seq(cache, block_table, lens, expected_tags)
+    _need(q, "q", BF16)
+    if q.shape[0] != block_table.shape[0] or q.shape[-1] != cache.head_dim:
+        raise ValueError("q must be [B][Hq][D] with the table's B and the cache's D")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", BF16)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if flags is not None:
+        _need(flags, "flags", U32)
+        if flags.numel() != block_table.shape[0]:
+            raise ValueError("flags must hold B words")
+    cd = cache.desc()
+    rc = lib().pa_decode_noalloc(ctypes.byref(cd), ctypes.byref(sd), q.shape[1], _ptr(q),
+                                 _ptr(out), float(softmax_scale), num_partitions, _ptr(flags),
+                                 _stream(stream))
+    if rc != 0:
+        raise PAError(rc, "pa_decode_noalloc")
+    return out
 
 
 def decode_step(cache, q, block_table, lens_old, n_new, k_new, v_new, lens, softmax_scale,

@@ -94,7 +94,8 @@ enum {
   PA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad enum */
   PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, page_size not 16, GQA group > 16 */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pa_decode_workspace_bytes */
-  PA_ERR_LAUNCH = -4       /* the HIP runtime refused a kernel launch */
+  PA_ERR_LAUNCH = -4,      /* the HIP runtime refused a kernel launch */
+  PA_ERR_SCRATCH = -5      /* pa_decode_noalloc: the call needs more than its static scratch */
 };
 
 /* Bits of the per-sequence flags word ([tags]: a request with any bit set is
@@ -221,6 +222,34 @@ int pa_decode_num_partitions(const pa_cache_desc *cache, const pa_seq_desc *seq,
 int pa_decode(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
               const uint16_t *q, uint16_t *out, float softmax_scale, int32_t num_partitions,
               uint32_t *flags, void *workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  Arguments, results, flags and error behaviour are
+ * those of pa_decode, with the same kernels and the same split.
+ *
+ * The split-K partials and the split plan live in a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES (32 MiB), which every GPU the library runs on
+ * holds until the process ends; its address is looked up once per device,
+ * on that device's first call.  The call allocates nothing and issues no
+ * memset: no scratch byte needs to start at zero, since every call writes
+ * each byte it reads before reading it.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (work on several
+ *     streams, or from several host threads at once) race and give wrong
+ *     results; calls ordered on one stream do not.
+ *   - Make the call with the stream's device current (PA_ERR_INVALID_ARG
+ *     otherwise).
+ *   - A call that needs more than PA_NOALLOC_SCRATCH_BYTES (what
+ *     pa_decode_workspace_bytes returns for the same arguments) returns
+ *     PA_ERR_SCRATCH before anything is enqueued; pa_decode with a caller's
+ *     workspace has no such limit.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
+                      const uint16_t *q, uint16_t *out, float softmax_scale,
+                      int32_t num_partitions, uint32_t *flags, pa_stream_t stream);
 
 /*
  * pa_decode, plus timing events recorded on `stream` around its kernels:
