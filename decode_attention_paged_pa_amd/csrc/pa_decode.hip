@@ -589,14 +589,32 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // exactly as from -inf.  Partials of such columns are never merged (the
   // reduce reads only partitions that hold a visible token of the row).
   constexpr float kEmptyMax = CAUSAL ? -3.40282347e38f : -INFINITY;
-  f32x4 o[NQ][NT];
+  // O^T accumulators.  One tile: 16 x 16 tiles (dims x columns), one per 16
+  // dims.  Several tiles: 32 x 32 tiles, one per (32 dims, pair of column
+  // tiles), for the double-rate 32x32x16 P.V MFMA -- a page's 16 tokens are
+  // exactly its K dimension (same register count: D / 2 per column tile).
+  // In a 32 x 32 tile lane l holds column 32 p + (l & 31) and the dims
+  // 32 J + 8 g + 4 (l >> 5) + r of element 4 g + r.
+  constexpr bool WIDE = NQ >= 2;
+  constexpr int NP = WIDE ? NQ / 2 : 1;        // column-tile pairs
+  constexpr int NJ = WIDE ? NT / 2 : 1;        // 32-dim blocks
+  f32x4 o[WIDE ? 1 : NQ][WIDE ? 1 : NT];
+  f32x16 ow[NP][NJ];
   float m_run[NQ], l_acc[NQ];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
+    if constexpr (!WIDE) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) o[nq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NT; ++j) o[nq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     m_run[nq] = kEmptyMax;
     l_acc[nq] = 0.f;
+  }
+  if constexpr (WIDE) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) ow[pp][jj] = f32x16{};
   }
 
   const int32_t* bt = a.block_table + (size_t)row * a.table_width + p0;
@@ -763,15 +781,32 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       grow |= lmax[nq] > m_run[nq] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      float alph[NQ];
+      bool moved[NQ];
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) {
-        if (__builtin_amdgcn_ballot_w64(lmax[nq] > m_run[nq] + kRescaleSlack)) {
+        alph[nq] = 1.f;
+        moved[nq] = __builtin_amdgcn_ballot_w64(lmax[nq] > m_run[nq] + kRescaleSlack) != 0;
+        if (moved[nq]) {
           const float m_new = fmaxf(m_run[nq], col_max(lmax[nq]));
           const float alpha = __builtin_amdgcn_exp2f(m_run[nq] - m_new);
           l_acc[nq] *= alpha;
+          if constexpr (!WIDE) {
 #pragma unroll
-          for (int j = 0; j < NT; ++j) o[nq][j] *= alpha;
+            for (int j = 0; j < NT; ++j) o[nq][j] *= alpha;
+          }
+          alph[nq] = alpha;
           m_run[nq] = m_new;
+        }
+      }
+      if constexpr (WIDE) {   // lanes with (l & 16) hold the pair's second tile's column
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          if (moved[2 * pp] || moved[2 * pp + 1]) {
+            const float f = pick_hi16(alph[2 * pp], alph[2 * pp + 1]);
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) ow[pp][jj] *= f;
+          }
         }
       }
     }
@@ -808,7 +843,38 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         for (int i = 0; i < NSEG; ++i) vr[i] &= u32x4{lo, hi, lo, hi};
       }
     }
-    if (FP8) {
+    if constexpr (WIDE) {
+      // 32x32x16: B = P^T of a pair of column tiles, A = V^T of 32 dims; both
+      // from the 16 x 16 operands of two tiles by one row swap per dword
+      u32x4 pb2[NP];
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        if (FP8) pb2[pp] = pair_rows(__builtin_bit_cast(u32x2, pbh[2 * pp]),
+                                     __builtin_bit_cast(u32x2, pbh[2 * pp + 1]));
+        else pb2[pp] = pair_rows(__builtin_bit_cast(u32x2, pbb[2 * pp]),
+                                 __builtin_bit_cast(u32x2, pbb[2 * pp + 1]));
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        u32x4 av;
+        if (FP8) {
+          av = pair_rows(fp8x4_to_f16x4(vr[(2 * jj) >> 2][(2 * jj) & 3]),
+                         fp8x4_to_f16x4(vr[(2 * jj + 1) >> 2][(2 * jj + 1) & 3]));
+        } else {   // tiles 2 jj and 2 jj + 1 are the two halves of segment jj
+          const u32x4& seg = vr[jj];
+          av = pair_rows(u32x2{seg[0], seg[1]}, u32x2{seg[2], seg[3]});
+        }
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          if (FP8)
+            ow[pp][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, pb2[pp]), ow[pp][jj], 0, 0, 0);
+          else
+            ow[pp][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb2[pp]), ow[pp][jj], 0, 0, 0);
+        }
+      }
+    } else if (FP8) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const uint32_t w = vr[j >> 2][j & 3];
@@ -842,35 +908,79 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // O = 0, and is written as zeros.  vfac converts O to the values' units
   // (FP8: v_ref / kPScale; 1 for BF16 and for a parked partition).
   auto emit = [&](int part, float vfac) {
+    if constexpr (WIDE) {
+      float lt[NQ];
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) {
-      const float l_tot = col_sum(l_acc[nq]);
-      const int cc = cbase + 16 * nq + c;
-      if (cc < cend) {
+      for (int nq = 0; nq < NQ; ++nq) lt[nq] = col_sum(l_acc[nq]);
+      const int dq = 4 * (lane >> 5);           // this lane's offset within each 8 dims
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const float l_tot = pick_hi16(lt[2 * pp], lt[2 * pp + 1]);
+        const float m_col = pick_hi16(m_run[2 * pp], m_run[2 * pp + 1]);
+        const int cc = cbase + 32 * pp + (lane & 31);
+        if (cc >= cend) continue;
         const size_t qrow = col_row(cc);
         if (direct) {
-          if (a.row_ml != nullptr && q4 == 0) {   // scored decode: the row's final (max, sum)
-            a.row_ml[qrow * 2 + 0] = m_run[nq];
-            a.row_ml[qrow * 2 + 1] = l_tot;
-          }
           const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : (FP8 ? vfac / l_tot : 1.f / l_tot);
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const f32x4 v = o[nq][j];
-            uint32_t lo = (uint32_t)bf16_rne(v[0] * inv) | ((uint32_t)bf16_rne(v[1] * inv) << 16);
-            uint32_t hi = (uint32_t)bf16_rne(v[2] * inv) | ((uint32_t)bf16_rne(v[3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
-          }
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x16& v = ow[pp][jj];
+              const uint32_t lo = (uint32_t)bf16_rne(v[4 * g] * inv) |
+                                  ((uint32_t)bf16_rne(v[4 * g + 1] * inv) << 16);
+              const uint32_t hi = (uint32_t)bf16_rne(v[4 * g + 2] * inv) |
+                                  ((uint32_t)bf16_rne(v[4 * g + 3] * inv) << 16);
+              *reinterpret_cast<u32x2*>(a.out + qrow * D + 32 * jj + 8 * g + dq) = u32x2{lo, hi};
+            }
         } else {
-          // fixed partitions: [row][Pn]; planned: [slot][column]
           const size_t pi = planned ? (size_t)pslot * C + cc : qrow * Pn + part;
           float* po = a.part_o + pi * D;
 #pragma unroll
-          for (int j = 0; j < NT; ++j)
-            *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = FP8 ? o[nq][j] * vfac : o[nq][j];
-          if (q4 == 0) {
-            a.part_ml[pi * 2 + 0] = m_run[nq];
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x16& v = ow[pp][jj];
+              const f32x4 x = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+              *reinterpret_cast<f32x4*>(po + 32 * jj + 8 * g + dq) = FP8 ? x * vfac : x;
+            }
+          if (dq == 0) {
+            a.part_ml[pi * 2 + 0] = m_col;
             a.part_ml[pi * 2 + 1] = l_tot;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) {
+        const float l_tot = col_sum(l_acc[nq]);
+        const int cc = cbase + 16 * nq + c;
+        if (cc < cend) {
+          const size_t qrow = col_row(cc);
+          if (direct) {
+            if (a.row_ml != nullptr && q4 == 0) {   // scored decode: the row's final (max, sum)
+              a.row_ml[qrow * 2 + 0] = m_run[nq];
+              a.row_ml[qrow * 2 + 1] = l_tot;
+            }
+            const float inv = (CAUSAL && !(l_tot > 0.f)) ? 0.f : (FP8 ? vfac / l_tot : 1.f / l_tot);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              const f32x4 v = o[nq][j];
+              uint32_t lo = (uint32_t)bf16_rne(v[0] * inv) | ((uint32_t)bf16_rne(v[1] * inv) << 16);
+              uint32_t hi = (uint32_t)bf16_rne(v[2] * inv) | ((uint32_t)bf16_rne(v[3] * inv) << 16);
+              *reinterpret_cast<u32x2*>(a.out + qrow * D + 16 * j + 4 * q4) = u32x2{lo, hi};
+            }
+          } else {
+            // fixed partitions: [row][Pn]; planned: [slot][column]
+            const size_t pi = planned ? (size_t)pslot * C + cc : qrow * Pn + part;
+            float* po = a.part_o + pi * D;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+              *reinterpret_cast<f32x4*>(po + 16 * j + 4 * q4) = FP8 ? o[nq][j] * vfac : o[nq][j];
+            if (q4 == 0) {
+              a.part_ml[pi * 2 + 0] = m_run[nq];
+              a.part_ml[pi * 2 + 1] = l_tot;
+            }
           }
         }
       }
@@ -915,10 +1025,17 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       if (vmax > v_ref) {
         if (v_ref > 0.f) {
           const float r = v_ref / vmax;
+          if constexpr (WIDE) {
 #pragma unroll
-          for (int nq = 0; nq < NQ; ++nq)
+            for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) o[nq][j] *= r;
+              for (int jj = 0; jj < NJ; ++jj) ow[pp][jj] *= r;
+          } else {
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+              for (int j = 0; j < NT; ++j) o[nq][j] *= r;
+          }
         }
         v_ref = vmax;
       }

@@ -8,6 +8,8 @@
 namespace pa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +87,30 @@ __device__ inline float col_max(float x) {
   x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+// The 32x32x16 MFMA operand (8 halves of one row or column: k = 8 (l >> 5) ..
+// + 7) from the 16x16x16 operands of two tiles a and b (4 halves each: lane
+// (c, q) holds k = 4 q .. 4 q + 3 of row or column c).  v_permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, so per dword the first result holds rows {a0, b0, a2, b2} and
+// the second {a1, b1, a3, b3}: lane l then holds k 0-7 (l < 32) or 8-15 of
+// row (or column) l & 31 -- a's rows for l & 16 clear, b's for it set.
+__device__ inline u32x4 pair_rows(u32x2 a, u32x2 b) {
+  auto s0 = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  auto s1 = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
+// a in lanes whose bit 4 is clear, b in the others (lanes 16-31 and 48-63:
+// the second column tile of a 32-column pair).  Written as one v_cndmask with
+// a constant lane mask: as a C++ select between two array elements the
+// compiler turned it into a lane-indexed stack array, whose reload waited
+// for every outstanding memory load.
+__device__ inline float pick_hi16(float a, float b) {
+  float r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(0xFFFF0000FFFF0000ull));
+  return r;
 }
 
 // Maximum over the 64 lanes of a wave (NaN inputs are ignored by fmaxf).
