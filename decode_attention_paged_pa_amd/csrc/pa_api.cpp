@@ -141,8 +141,8 @@ Split prefill_split(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq, in
 Split mass_split(const pa_cache_desc* c, const pa_seq_desc* s);
 
 struct WorkspaceLayout {
-  size_t part_o = 0, part_ml = 0, plan = 0, plan_group = 0, row_ml = 0;
-  size_t mass_plan = 0, mass_group = 0, total = 0;
+  size_t part_o = 0, part_ml = 0, plan = 0, plan_group = 0, plan_rec = 0, row_ml = 0;
+  size_t mass_plan = 0, mass_group = 0, unit_flags = 0, total = 0;
 };
 
 WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
@@ -159,12 +159,18 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* c, const pa_seq_desc* s, i
     off += align256(((size_t)sp.groups + 3) * sizeof(int32_t));
     w.plan_group = off;
     off += align256((size_t)sp.max_pairs * sizeof(int32_t));
+    w.plan_rec = off;
+    off += align256((size_t)sp.max_pairs * 4 * sizeof(int32_t));
   } else if (sp.parts > 1) {
     const size_t rows = (size_t)s->batch * q_len * hq * sp.parts;
     w.part_o = off;
     off += align256(rows * c->head_dim * sizeof(float));
     w.part_ml = off;
     off += align256(rows * 2 * sizeof(float));
+  }
+  if (c->layout == PA_LAYOUT_HEAD) {   // the validation's word per unit
+    w.unit_flags = off;
+    off += align256((size_t)s->batch * c->num_kv_heads * sizeof(uint32_t));
   }
   if (scored) {
     w.row_ml = off;
@@ -330,24 +336,31 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   };
 
   rec(0);
+  char* ws = static_cast<char*>(workspace);
+  // HEAD layout: one validation workgroup and word per unit; the decode ORs a
+  // sequence's words and its last kernel writes flags[b]
+  const bool per_unit = flags && head;
+  uint32_t* unit_flags = per_unit ? reinterpret_cast<uint32_t*>(ws + wl.unit_flags) : nullptr;
   pa::ValidateArgs v{};
   if (flags) {
     v.block_table = seq->block_table;
     v.lens = seq->lens;
     v.expected_tags = seq->expected_tags;
     v.page_tags = cache->page_tags;
-    v.flags = flags;
+    v.flags = per_unit ? unit_flags : flags;
     v.batch = seq->batch;
     v.num_kv_heads = cache->num_kv_heads;
     v.table_width = seq->table_width;
     v.num_pages = cache->num_pages;
     v.head_layout = head;
+    v.per_unit = per_unit;
+    v.rows = per_unit ? seq->batch * cache->num_kv_heads : seq->batch;
   }
-  char* ws = static_cast<char*>(workspace);
   // the decode's split (automatic) and the score pass's split (scored decode)
   const Split ms = scores ? mass_split(cache, seq) : Split{};
-  const pa::PlanArgs pl = plan_args(seq, sp, ws + wl.plan, ws + wl.plan_group, (int)kPlanWaves,
+  pa::PlanArgs pl = plan_args(seq, sp, ws + wl.plan, ws + wl.plan_group, (int)kPlanWaves,
                                     kPlanMinChunk, seq->table_width);
+  if (sp.planned) pl.plan_rec = reinterpret_cast<int32_t*>(ws + wl.plan_rec);
   const pa::PlanArgs pm = plan_args(seq, ms, ws + wl.mass_plan, ws + wl.mass_group,
                                     kMassPlanWaves, kMassMinChunk, pa::kMassRun);
   if (pa::launch_prep(flags ? &v : nullptr, sp.planned ? &pl : nullptr, scores ? &pm : nullptr,
@@ -363,6 +376,8 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.block_table = seq->block_table;
   a.lens = seq->lens;
   a.flags = flags;
+  a.unit_flags = unit_flags;
+  a.flags_out = flags;
   a.q = q;
   a.out = out;
   if (sp.planned || sp.parts > 1) {
@@ -372,6 +387,7 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   if (sp.planned) {
     a.plan = reinterpret_cast<const int32_t*>(ws + wl.plan);
     a.plan_group = reinterpret_cast<const int32_t*>(ws + wl.plan_group);
+    a.plan_rec = reinterpret_cast<const int32_t*>(ws + wl.plan_rec);
     a.max_pairs = sp.max_pairs;
   }
   if (scores) a.row_ml = reinterpret_cast<float*>(ws + wl.row_ml);
@@ -395,10 +411,13 @@ int decode_impl(const pa_cache_desc* cache, const pa_seq_desc* seq, int32_t num_
   a.xcd_order = 0;
 #endif
   a.score_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  const bool reduce = sp.planned || sp.parts > 1;
+  a.write_flags = (per_unit && !reduce) ? 1 : 0;   // the decode's last kernel writes flags[b]
   if (pa::launch_attention(a, cache->head_dim, fp8, head, stream) != hipSuccess)
     return PA_ERR_LAUNCH;
   rec(2);
-  if (sp.planned || sp.parts > 1) {
+  if (reduce) {
+    a.write_flags = per_unit ? 1 : 0;
     if (pa::launch_reduce(a, cache->head_dim, head, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (scores) {   // second pass: K again, with the rows' final (max, sum)

@@ -125,27 +125,33 @@ __device__ inline u32x4 load16(const uint8_t* p) {
 }
 
 // ------------------------------------------------------------ validation
-// One workgroup per sequence; integrity check of the pages it will read
-// ("Cloudflare quantizes Kimi and GLM caches for 41% faster inference",
-// integrity-check paragraph: a separate batch validation before decode reads).
-// The table entries of all the sequence's units (HEAD: one per KV head) form
-// one flat index space, 8 entries per thread per pass with every load of a
-// pass issued before any is used: two dependent round trips per 8192 entries,
-// whatever the number of units.
+// Integrity check of the pages a decode will read ("Cloudflare quantizes
+// Kimi and GLM caches for 41% faster inference", integrity-check paragraph:
+// a separate batch validation before decode reads).  One workgroup per
+// sequence writes its flags word; in the HEAD layout with per_unit, one
+// workgroup per unit writes a word per unit instead, and the decode ORs a
+// sequence's words (a HEAD sequence has Hkv tables of up to table_width
+// entries each: spread over Hkv workgroups the check takes one pass, where a
+// workgroup per sequence took several, measured 4.5% of the headwise step).
+// The table entries of the workgroup's units form one flat index space, 8
+// entries per thread per pass with every load of a pass issued before any is
+// used: two dependent round trips per 8192 entries.
 constexpr int kValUnits = 64;   // units whose entry offsets are held at a time
 
-__device__ void validate_block(const ValidateArgs& a, int b) {
+__device__ void validate_block(const ValidateArgs& a, int x) {
+  const int b = a.per_unit ? x / a.num_kv_heads : x;
+  const int unit_base = a.per_unit ? x : b * a.num_kv_heads;   // HEAD: first unit
   __shared__ uint32_t s_bits;
   __shared__ int s_off[kValUnits + 1];
   const int tid = threadIdx.x;
   if (tid == 0) s_bits = 0;
   uint32_t bits = 0;
   const int cap = a.table_width * kPageSize;
-  const int n_units = a.head_layout ? a.num_kv_heads : 1;
+  const int n_units = (a.head_layout && !a.per_unit) ? a.num_kv_heads : 1;
   for (int u0 = 0; u0 < n_units; u0 += kValUnits) {
     const int nu = min(kValUnits, n_units - u0);
     if (tid < nu) {
-      const int row = a.head_layout ? b * a.num_kv_heads + u0 + tid : b;
+      const int row = a.head_layout ? unit_base + u0 + tid : b;
       int L = a.lens[row];
       if (L > cap || L < 0) bits |= 4u;
       L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -185,7 +191,7 @@ __device__ void validate_block(const ValidateArgs& a, int b) {
         want[j] = 0u;
         if (i < total) {
           const int u = unit_of(i);               // the unit holding flat entry i
-          const int row = a.head_layout ? b * a.num_kv_heads + u0 + u : b;
+          const int row = a.head_layout ? unit_base + u0 + u : b;
           const size_t e = (size_t)row * a.table_width + (i - s_off[u]);
           pid[j] = a.block_table[e];
           if (a.expected_tags) want[j] = a.expected_tags[e];
@@ -205,7 +211,7 @@ __device__ void validate_block(const ValidateArgs& a, int b) {
   }
   if (bits) atomicOr(&s_bits, bits);  // LDS atomic
   __syncthreads();
-  if (tid == 0) a.flags[b] = s_bits;
+  if (tid == 0) a.flags[x] = s_bits;
 }
 
 // ----------------------------------------------------------------- plan
@@ -322,7 +328,13 @@ __device__ void plan_block(const PlanArgs& a) {
     const int excl = s_carry + s_wave[wv] + incl - parts;
     if (g < n) {
       first[g] = excl;
-      for (int p = 0; p < parts && excl + p < a.max_pairs; ++p) a.plan_group[excl + p] = g;
+      int L = a.lens[g];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      for (int p = 0; p < parts && excl + p < a.max_pairs; ++p) {
+        a.plan_group[excl + p] = g;
+        if (a.plan_rec)
+          *reinterpret_cast<int4*>(a.plan_rec + 4 * (excl + p)) = int4{g, p, chunk, L};
+      }
     }
     __syncthreads();
     if (tid == 1023) s_carry = excl + parts;
@@ -333,6 +345,15 @@ __device__ void plan_block(const PlanArgs& a) {
     a.plan[1] = min(s_carry, a.max_pairs);   // never clipped: max_pairs bounds the count
     first[n] = s_carry;
   }
+  if (a.plan_rec)   // slots past the last pair: no work
+    for (int p = s_carry + tid; p < a.max_pairs; p += 1024) a.plan_rec[4 * p] = -1;
+}
+
+// OR over the 64 lanes of a wave.
+__device__ inline uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x |= (uint32_t)__shfl_xor((int)x, d, 64);
+  return x;
 }
 
 // The validation and the plans share one launch: workgroups 0 .. nval - 1
@@ -426,6 +447,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   int chunk = a.chunk_pages;
   bool direct = Pn == 1;   // no reduce follows for this wave's unit: it writes the output rows
   int pslot = 0;           // planned: this wave's partial slot
+  int planned_len = 0;     // planned: the group's length (clamped), from its record
   if (planned) {
     // One partition per pair, all of about the same size; the workgroup
     // order (XCD-aware for SEQ, as below) is the same, over the plan's pairs.
@@ -441,12 +463,14 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       pair = item / hpg;
       hh = item - pair * hpg;
     }
-    if (pair >= a.plan[1]) return;
-    chunk = a.plan[0];
-    const int grp = a.plan_group[pair];
-    const int first = a.plan[2 + grp];
-    g = pair - first;
-    direct = a.plan[3 + grp] - first == 1;
+    if (pair >= a.max_pairs) return;
+    const int4 rec = *reinterpret_cast<const int4*>(a.plan_rec + 4 * pair);
+    const int grp = __builtin_amdgcn_readfirstlane(rec.x);
+    if (grp < 0) return;
+    g = __builtin_amdgcn_readfirstlane(rec.y);
+    chunk = __builtin_amdgcn_readfirstlane(rec.z);
+    planned_len = __builtin_amdgcn_readfirstlane(rec.w);
+    direct = (planned_len + kPageSize - 1) / kPageSize <= chunk;   // the group's only partition
     b = HEAD ? grp / Hkv : grp;
     h = HEAD ? grp - b * Hkv : hh;
     pslot = pair * hpg + hh;
@@ -532,7 +556,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int q4 = lane >> 4;     // which quarter of the MFMA K dimension
 
   const int cap = a.table_width * kPageSize;
-  int L = a.lens[row];
+  int L = planned ? planned_len : a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   int npages = (L + kPageSize - 1) / kPageSize;
   if (CAUSAL) {  // the block's last column sees L - T + t_last + 1 tokens
@@ -541,7 +565,16 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   }
   const int p0 = part0 * chunk;
   const int p1 = planned ? min(p0 + chunk, npages) : min(min(part0 + ppw, Pn) * chunk, npages);
-  const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
+  bool flagged;
+  if (a.unit_flags != nullptr) {   // HEAD with the check: the sequence's unit words
+    uint32_t word = 0u;
+    for (int u = lane; u < Hkv; u += 64) word |= a.unit_flags[(size_t)b * Hkv + u];
+    word = wave_or(word);
+    flagged = word != 0u;
+    if (a.write_flags && h == 0 && part0 == 0 && cb == 0 && lane == 0) a.flags_out[b] = word;
+  } else {
+    flagged = a.flags != nullptr && a.flags[b] != 0u;
+  }
   // query row (in [B][T][Hq]) of column cc of this unit
   auto col_row = [&](int cc) {
     const int t = cc / G;
@@ -1163,7 +1196,15 @@ __global__ __launch_bounds__(PA_RED_THREADS) void reduce_kernel(AttnArgs a) {
     step = (size_t)hpg * C;
   }
   const int nvp = min(nparts, (npages + chunk - 1) / chunk);
-  const bool flagged = a.flags != nullptr && a.flags[b] != 0u;
+  bool flagged;
+  if (a.unit_flags != nullptr) {   // HEAD with the check: the sequence's unit words
+    uint32_t word = 0u;
+    for (int u = 0; u < a.num_kv_heads; ++u) word |= a.unit_flags[(size_t)b * a.num_kv_heads + u];
+    flagged = word != 0u;
+    if (a.write_flags && rem == 0 && d0 == 0) a.flags_out[b] = word;   // the sequence's first row
+  } else {
+    flagged = a.flags != nullptr && a.flags[b] != 0u;
+  }
   uint16_t* orow = a.out + (size_t)qrow * D + d0;
   if (flagged || nvp == 0) {
     *reinterpret_cast<u32x2*>(orow) = u32x2{0u, 0u};
@@ -1485,7 +1526,7 @@ hipError_t launch_mass_t(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_prep(const ValidateArgs* v, const PlanArgs* p0, const PlanArgs* p1,
                        const AppendArgs* app, hipStream_t s) {
   if (!p0 && p1) return launch_prep(v, p1, nullptr, app, s);
-  const int nval = v ? v->batch : 0;
+  const int nval = v ? v->rows : 0;
   const int nplan = (p0 ? 1 : 0) + (p1 ? 1 : 0);
   const int64_t items = app ? (int64_t)app->batch * app->num_kv_heads * app->pages_per_unit : 0;
   const ValidateArgs va = v ? *v : ValidateArgs{};

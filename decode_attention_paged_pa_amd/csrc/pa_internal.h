@@ -21,7 +21,13 @@ struct AttnArgs {
   const float* v_scale;      // FP8 only
   const int32_t* block_table;
   const int32_t* lens;
-  const uint32_t* flags;     // nullptr: nothing flagged
+  const uint32_t* flags;     // nullptr: nothing flagged; SEQ: per sequence
+  // HEAD layout with the check on: one validation word per unit (the
+  // sequence is flagged when any of its Hkv words is), and the sequence
+  // words are written out by the last kernel of the decode (flags_out).
+  const uint32_t* unit_flags;
+  uint32_t* flags_out;
+  int write_flags;           // this kernel writes flags_out[b] = OR of the unit words
   const uint16_t* q;         // [B][q_len][Hq][D]
   uint16_t* out;             // [B][q_len][Hq][D]; written directly when num_parts == 1
   float* part_o;             // [B][q_len][Hq][Pn][D] unnormalised outputs
@@ -44,6 +50,10 @@ struct AttnArgs {
   // pair * heads_per_group + head.
   const int32_t* plan;
   const int32_t* plan_group;
+  // plan_rec[4 pair ..]: (group, partition within it, chunk, the group's
+  // length) of each pair slot < max_pairs, group -1 past the last pair: what
+  // an attention wave needs, in one load instead of three dependent ones.
+  const int32_t* plan_rec;
   int max_pairs;
 };
 
@@ -52,6 +62,7 @@ struct PlanArgs {
   const int32_t* lens;       // one length per group
   int32_t* plan;             // as AttnArgs::plan
   int32_t* plan_group;
+  int32_t* plan_rec;         // as AttnArgs::plan_rec; may be null
   int num_groups, heads_per_group, table_width, max_pairs;
   int target_waves, min_chunk, max_chunk;
 };
@@ -61,9 +72,11 @@ struct ValidateArgs {
   const int32_t* lens;
   const uint32_t* expected_tags;  // nullptr: range and length checks only
   const uint32_t* page_tags;
-  uint32_t* flags;
+  uint32_t* flags;                // per sequence, or per unit with per_unit
   int batch, num_kv_heads, table_width, num_pages;
   bool head_layout;
+  bool per_unit;                  // HEAD: one workgroup and one word per unit
+  int rows;                       // workgroups: batch, or batch * num_kv_heads with per_unit
 };
 
 struct AppendArgs {

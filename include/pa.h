@@ -173,13 +173,15 @@ int pa_cache_append(const pa_cache_desc *cache, const pa_seq_desc *seq, const in
 /*
  * Bytes of device workspace pa_decode needs for this shape and partition
  * count (0 = the library's choice).  0 when the decode needs none (one
- * partition per unit).  Returns (size_t)-1 for invalid arguments.
+ * partition per unit, SEQ layout).  Returns (size_t)-1 for invalid arguments.
+ * The HEAD layout always adds one uint32 per unit (B * Hkv, rounded up to
+ * 256 bytes) for the tag check, which validates each unit on its own.
  * With the automatic, length-balanced split (num_partitions 0, table_width
  * above 32) the size is the most any lengths can need: partials for
  * ceil(2048 / h) + groups (group, partition) pairs, where a group is a
  * sequence holding h = Hkv heads (SEQ) or one unit with h = 1 (HEAD), each
- * head G columns of D + 2 floats, plus the split plan: (groups + 3) and
- * (pairs) int32, every block rounded up to 256 bytes.
+ * head G columns of D + 2 floats, plus the split plan: (groups + 3),
+ * (pairs) and (4 * pairs) int32, every block rounded up to 256 bytes.
  */
 size_t pa_decode_workspace_bytes(const pa_cache_desc *cache, const pa_seq_desc *seq,
                                  int32_t num_q_heads, int32_t num_partitions);

@@ -174,12 +174,14 @@ def test_partition_choice():
     pairs = 2048 // 8 + 64                                  # SEQ: a pair holds the 8 heads of a sequence
     slots = pairs * 8 * 8
     assert ws(c, _seq(batch=64, table_width=2048)) == (
-        a256(slots * 128 * 4) + a256(slots * 8) + a256((64 + 3) * 4) + a256(pairs * 4))
+        a256(slots * 128 * 4) + a256(slots * 8) + a256((64 + 3) * 4) + a256(pairs * 4)
+        + a256(pairs * 16))                                 # a record per pair slot
     ch = _cache(layout=1)                                   # HEAD: a pair is one unit's partition
     pairs = 2048 + 16 * 8
     slots = pairs * 4
     assert ws(ch, _seq(batch=16, table_width=2048), hq=32) == (
-        a256(slots * 128 * 4) + a256(slots * 8) + a256((16 * 8 + 3) * 4) + a256(pairs * 4))
+        a256(slots * 128 * 4) + a256(slots * 8) + a256((16 * 8 + 3) * 4) + a256(pairs * 4)
+        + a256(pairs * 16) + a256(16 * 8 * 4))              # HEAD: one validation word per unit
 
 
 def _decode_multi(cache, seq, hq=32, q_len=4, q=FAKE, out=FAKE, scale=0.088, parts=0, flags=None,
