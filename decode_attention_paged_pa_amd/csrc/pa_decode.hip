@@ -243,6 +243,7 @@ __device__ void plan_block(const PlanArgs& a) {
   __shared__ int s_wave[16];
   __shared__ int s_carry;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (a.plan == nullptr || a.plan_group == nullptr) return;   // no plan asked of this workgroup
   const int n = a.num_groups;
   const int cap = a.table_width * kPageSize;
   auto pages = [&](int g) {
