@@ -63,6 +63,7 @@ size_t elem_bytes(const pa_cache_desc* c) { return c->kv_dtype == PA_KV_FP8_E4M3
 // cache faster than 4096 shorter ones, so small partitions are grouped until
 // the grid drops to that size.
 constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kSharedTargetGroups = 1536;   // prefill page-sharing workgroups: 2 rounds of 3 per CU
 
 void choose_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t req,
                        int* chunk_pages, int* num_parts, int* parts_per_wave) {
@@ -218,7 +219,8 @@ Split mass_split(const pa_cache_desc* c, const pa_seq_desc* s) {
 // when the grid would otherwise be small.
 int prefill_col_blocks(const pa_cache_desc* c, int32_t hq, int32_t q_len) {
   const int64_t cols = (int64_t)(hq / c->num_kv_heads) * q_len;
-  return (int)((cols + pa::kMaxCols - 1) / pa::kMaxCols);
+  if (cols <= pa::kMaxCols) return 1;   // one multi-query wave holds the unit's columns
+  return (int)((cols + pa::kPrefillCols - 1) / pa::kPrefillCols);
 }
 
 void choose_prefill_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int32_t hq,
@@ -226,8 +228,18 @@ void choose_prefill_partitions(const pa_cache_desc* c, const pa_seq_desc* s, int
   const int W = s->table_width;
   int parts = req;
   if (req <= 0) {
-    const int64_t waves = (int64_t)s->batch * c->num_kv_heads * prefill_col_blocks(c, hq, q_len);
-    int64_t p = (kTargetWaves + waves - 1) / waves;
+    // Work items: waves of 64 columns; with the page-sharing kernel (blocks
+    // of 32 columns), workgroups of kWaves blocks, aiming at two rounds of the
+    // 3 resident per CU.  Measured on MI355X (512-token chunk over 0-30K
+    // prefixes, 512 workgroups): 1, 2, 3, 4 and 6 partitions took 1346, 729,
+    // 551, 738 and 573 us; the 2048-token chunk (2048 workgroups) is fastest
+    // unsplit.
+    const int64_t cb = prefill_col_blocks(c, hq, q_len);
+    const bool shared = pa::kPrefillCols == 32 && cb > 1;
+    const int64_t items = (int64_t)s->batch * c->num_kv_heads *
+                          (shared ? (cb + pa::kWaves - 1) / pa::kWaves : cb);
+    const int64_t target = shared ? kSharedTargetGroups : kTargetWaves;
+    int64_t p = (target + items - 1) / items;
     const int64_t pmax = (W + 31) / 32;               // partitions of at least 32 pages
     parts = (int)(p < 1 ? 1 : (p > pmax ? pmax : p));
   }

@@ -95,6 +95,13 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #ifndef PA_MQ_WAVES4
 #define PA_MQ_WAVES4 2         // occupancy hint with 4 column tiles
 #endif
+#ifndef PA_SHARED_WAVES
+#define PA_SHARED_WAVES 3      // occupancy hint of the page-sharing kernel
+#endif
+#ifndef PA_SHARED_STAGES
+#define PA_SHARED_STAGES 4     // LDS pages of the page-sharing kernel's ring (3 in flight)
+#endif
+static_assert(PA_SHARED_STAGES >= 3 && PA_SHARED_STAGES <= 6, "page-sharing ring");
 constexpr int kPipe = PA_PIPE_DEPTH;
 static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
 static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
@@ -103,15 +110,16 @@ static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
 // one wave per SIMD less than the FP8 one instead of spilling; every extra
 // tile of query columns adds its O accumulators and Q operands (D/2 + D/4
 // registers per lane at D = 128... 48 + 16 at D = 64), paid for in waves.
-template <bool FP8, int NQ>
+template <bool FP8, int NQ, bool SHARED = false>
 constexpr int waves_per_eu() {
-  return NQ == 1 ? (FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)
+  return SHARED ? PA_SHARED_WAVES
+       : NQ == 1 ? (FP8 ? PA_WAVES_PER_EU : PA_WAVES_PER_EU - 1)
        : NQ == 2 ? (PA_MQ_WAVES2 > 0 ? PA_MQ_WAVES2
                                      : (FP8 ? PA_WAVES_PER_EU - 1 : PA_WAVES_PER_EU - 2))
                  : PA_MQ_WAVES4;
 }
 #if PA_WAVES_PER_EU > 0
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(waves_per_eu<FP8, NQ>())))
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(waves_per_eu<FP8, NQ, SHARED>())))
 #else
 #define PA_OCCUPANCY
 #endif
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(AppendArgs ap, int item
 //
 // With a.row_ml set (scored decode), single-partition rows also keep their
 // final (max, sum) there for the eviction score pass (mass_kernel below).
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SHARED>
 __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
   constexpr int E = FP8 ? 1 : 2;               // bytes per cached element
   constexpr int BLOCK = kPageSize * D * E;     // bytes of one (page, head) block
@@ -427,9 +435,20 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   __shared__ float s_stash[kWaves][kStash][64];
   // With several column tiles the Q operands live in LDS instead of
   // registers (D/8 registers per tile per lane otherwise): each lane reads
-  // back only what it wrote itself, so no barrier is involved.
-  constexpr bool QLDS = NQ > 1;
+  // back only what it wrote itself, so no barrier is involved.  The
+  // page-sharing kernel (SHARED, below) keeps its two tiles' Q in registers
+  // and gives LDS to the pages.
+  static_assert(!SHARED || (NQ == 2 && CAUSAL), "page sharing: prefill column blocks of 32");
+  constexpr bool QLDS = NQ > 1 && !SHARED;
   __shared__ bf16x8 s_q[QLDS ? kWaves : 1][QLDS ? NQ * NSTEP : 1][64];
+  // SHARED: a ring of pages (K then V, 1 KiB segments) for the workgroup,
+  // one array per stage, so that the compiler tells the stages apart and
+  // waits for a stage's loads only where that stage is read.
+  constexpr int kStages = SHARED ? PA_SHARED_STAGES : 1;
+  constexpr int kRingSegs = SHARED ? 2 * NSEG : 1;
+  __shared__ u32x4 s_st0[kRingSegs][64], s_st1[kStages > 1 ? kRingSegs : 1][64],
+      s_st2[kStages > 2 ? kRingSegs : 1][64], s_st3[kStages > 3 ? kRingSegs : 1][64],
+      s_st4[kStages > 4 ? kRingSegs : 1][64], s_st5[kStages > 5 ? kRingSegs : 1][64];
 
   const int Pn = a.num_parts;
   const bool planned = a.plan != nullptr;      // length-balanced split (see plan_block)
@@ -499,14 +518,19 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     // Dealt across XCDs instead, each L2 saw every unit and hit 43% of its
     // requests (measured on the 2048-token chunk).  Within a unit the blocks
     // that see the most pages start first.
+    // SHARED: a workgroup is kWaves consecutive column blocks of one (unit,
+    // partition group), and all its waves stay to the end (they share the
+    // page loads and a barrier per page), also those past the unit's columns.
     const int per = cblocks * groups;               // waves of one unit
-    const int wgu = (per + kWaves - 1) / kWaves;    // workgroups of one unit
+    const int cgroups = (cblocks + kWaves - 1) / kWaves;
+    const int wgu = SHARED ? cgroups * groups : (per + kWaves - 1) / kWaves;   // workgroups of one unit
     const int x = blockIdx.x;
     const int k = x >> 3;
     const int slot = (k / wgu) * 8 + (x & 7);       // the unit's place in the start order
-    const int j = (k - (k / wgu) * wgu) * kWaves + wave;   // wave within the unit
+    const int jw = k - (k / wgu) * wgu;             // workgroup within the unit
+    const int j = jw * kWaves + wave;               // wave within the unit
     const int nunits = a.batch * Hkv;
-    if (slot >= nunits || j >= per) return;
+    if (slot >= nunits || (!SHARED && j >= per)) return;   // (SHARED: uniform over the workgroup)
     // The longest units start first: a unit's waves are as long as its
     // cached prefix, and one that starts after the short units have drained
     // ends the launch late (measured on MI355X: 4% on the 2048-token chunk
@@ -532,9 +556,15 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         unit = HEAD ? key : key * Hkv + (slot - want * Hkv);
       }
     }
-    const int jb = j / groups;
-    g = j - jb * groups;
-    cb = cblocks - 1 - jb;
+    if constexpr (SHARED) {
+      const int jg = jw / groups;
+      g = jw - jg * groups;
+      cb = (cgroups - 1 - jg) * kWaves + wave;      // may be past the last block: no columns
+    } else {
+      const int jb = j / groups;
+      g = j - jb * groups;
+      cb = cblocks - 1 - jb;
+    }
     b = unit / Hkv;
     h = unit - b * Hkv;
   } else {
@@ -548,7 +578,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     h = unit - b * Hkv;
   }
   const int cbase = cb * 16 * NQ;              // first column of this wave's block
-  const int cend = min(cbase + 16 * NQ, C);
+  const int cend = max(min(cbase + 16 * NQ, C), cbase);   // (= cbase: a block past the columns)
   const int unit = b * Hkv + h;
   const int part0 = g * ppw;  // first partition of this wave
   const int row = HEAD ? unit : b;
@@ -559,11 +589,17 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int cap = a.table_width * kPageSize;
   int L = planned ? planned_len : a.lens[row];
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  int npages = (L + kPageSize - 1) / kPageSize;
-  if (CAUSAL) {  // the block's last column sees L - T + t_last + 1 tokens
-    const int seen = L - T + (cend - 1) / G + 1;
-    npages = seen > 0 ? min(npages, (seen + kPageSize - 1) / kPageSize) : 0;
-  }
+  const int npages_all = (L + kPageSize - 1) / kPageSize;
+  auto pages_to = [&](int ce) {  // pages visible to the column before ce (CAUSAL)
+    const int seen = L - T + (ce - 1) / G + 1;  // column ce - 1 sees L - T + t + 1 tokens
+    return seen > 0 ? min(npages_all, (seen + kPageSize - 1) / kPageSize) : 0;
+  };
+  // SHARED: the workgroup walks the pages its last column sees; each wave
+  // computes the ones its own columns see (npages_w), none without columns.
+  const int wg_cend = SHARED ? min((cb - wave + kWaves) * 16 * NQ, C) : cend;
+  int npages = npages_all;
+  if (CAUSAL) npages = pages_to(SHARED ? wg_cend : cend);
+  const int npages_w = !SHARED ? npages : (cend > cbase ? pages_to(cend) : 0);
   const int p0 = part0 * chunk;
   const int p1 = planned ? min(p0 + chunk, npages) : min(min(part0 + ppw, Pn) * chunk, npages);
   bool flagged;
@@ -589,6 +625,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     return;
   }
   const int n = p1 - p0;
+  const int nw = SHARED ? max(min(p1, npages_w) - p0, 0) : n;   // pages this wave computes
 
   // Q^T as the B operand of S^T = K Q^T: lane (c, q4) of tile nq holds column
   // 16 * nq + c and the 8 dims that the K A-operand places in this lane for
@@ -1078,6 +1115,105 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       for (int j = 0; j < kIdRegs; ++j) svs[j] *= to_op;
     }
     id_chunk = 0;
+    if constexpr (SHARED) {
+      // The workgroup's waves load each page once, into LDS, for all of
+      // them: wave w requests 1 KiB segments w, w + kWaves, ... of the page
+      // (K's, then V's) straight into the page's ring stage, kStages - 1
+      // pages ahead.  Page r: each wave waits for its own segments of it
+      // (the counter runs in order: only later pages' may stay in flight),
+      // then a barrier makes the stage whole for all and proves that every
+      // wave has read the previous page, whose stage the next request
+      // reuses.  Each lane requests the chunk that the compute lane of its
+      // index reads, so the LDS reads are linear.  Every wave runs all of
+      // the workgroup's pages (m: uniform) and computes those its own
+      // columns see (mw).
+      constexpr int SEGS = 2 * NSEG;
+      constexpr int MY = (SEGS + kWaves - 1) / kWaves;   // segments per wave and page
+      constexpr int R = kStages;
+      auto ring = [&](auto st) -> u32x4 (*)[64] {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S == 0) return s_st0;
+        else if constexpr (S == 1) return s_st1;
+        else if constexpr (S == 2) return s_st2;
+        else if constexpr (S == 3) return s_st3;
+        else if constexpr (S == 4) return s_st4;
+        else return s_st5;
+      };
+      float stk[R], stv[R];   // FP8 scales of the pages in the ring
+      auto request = [&](auto st, int r) {   // page r into stage st
+        constexpr int S = decltype(st)::value;
+        const int pid = page_id(r);
+        const uint8_t* kp = kpool + (size_t)pid * page_stride;
+        const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
+        const uint8_t* vp = vpool + (size_t)vpid * page_stride;
+        u32x4 (*dst)[64] = ring(st);
+#pragma unroll
+        for (int i = 0; i < MY; ++i) {
+          const int sg = wave + i * kWaves;
+          if (sg < SEGS) {
+            const uint8_t* src = (sg < NSEG ? kp + sg * 1024 : vp + (sg - NSEG) * 1024) + lane_off;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)src,
+                (__attribute__((address_space(3))) void*)&dst[sg][0], 16, 0, 0);
+          }
+        }
+        if constexpr (SEGSC) {
+          stk[S] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), r & 63));
+          stv[S] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), r & 63));
+        }
+      };
+      // every wave's reads of the ring are done (lgkmcnt), then the barrier;
+      // the compiler-only fences keep LDS accesses on their side of it
+      auto sync = [&]() {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // s_waitcnt lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      };
+      const int mw = min(max(nw - seg, 0), m);
+      sync();                                             // the last segment's reads are done
+      auto first = [&](auto jc) {   // pages 0 .. R - 2 into stages 0 .. R - 2
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J + 1 < R) {
+          if (J < m) request(IntC<J>{}, J);
+        }
+      };
+      first(IntC<0>{});
+      first(IntC<1>{});
+      first(IntC<2>{});
+      first(IntC<3>{});
+      first(IntC<4>{});
+      for (int r0 = 0; r0 < m; r0 += R) {
+        auto step = [&](auto uc) {
+          constexpr int U = decltype(uc)::value;
+          const int r = r0 + U;
+          if (r >= m) return;
+          // pages requested after page r: r + 1 .. min(r + R - 2, m - 1)
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (r + R - 2 < m) __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));  // vmcnt
+          else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
+          sync();
+          if (r + R - 1 < m) request(IntC<(U + R - 1) % R>{}, r + R - 1);
+          if (r < mw) {
+            u32x4 (*src)[64] = ring(IntC<U>{});
+            u32x4 kp[NSEG], vp[NSEG];
+#pragma unroll
+            for (int i = 0; i < NSEG; ++i) {
+              kp[i] = src[i][lane];
+              vp[i] = src[NSEG + i][lane];
+            }
+            compute(kp, vp, stk[U], stv[U], seg + r);
+          }
+        };
+        step(IntC<0>{});
+        step(IntC<1>{});
+        step(IntC<2>{});
+        if constexpr (R > 3) step(IntC<3>{});
+        if constexpr (R > 4) step(IntC<4>{});
+        if constexpr (R > 5) step(IntC<5>{});
+      }
+      continue;
+    }
     if constexpr (LATEK) {
       // One K buffer: page r+1 is requested as soon as page r's Q.K has read
       // K, and the waits are the compiler's (K before Q.K, V before P.V)
@@ -1261,7 +1397,7 @@ __global__ __launch_bounds__(PA_RED_THREADS) void reduce_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL>
+template <int D, bool FP8, bool HEAD, int NQ, bool CAUSAL, bool SHARED = false>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   unsigned grid;
   if (a.plan != nullptr) {  // enough waves for the most pairs a plan can hold; the rest exit
@@ -1275,7 +1411,8 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
       const unsigned pairs = (unsigned)a.batch * groups;
       grid = ((pairs + 7) / 8) * 8 * (unsigned)(a.num_kv_heads / kWaves);
     } else if (a.col_blocks > 1) {  // see attention_kernel: a unit's workgroups on one XCD
-      const unsigned wgu = ((unsigned)a.col_blocks * groups + kWaves - 1) / kWaves;
+      const unsigned wgu = SHARED ? ((unsigned)(a.col_blocks + kWaves - 1) / kWaves) * groups
+                                  : ((unsigned)a.col_blocks * groups + kWaves - 1) / kWaves;
       const unsigned units = (unsigned)a.batch * a.num_kv_heads;
       grid = ((units + 7) / 8) * 8 * wgu;
     } else {
@@ -1283,7 +1420,7 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
       grid = (items + kWaves - 1) / kWaves;
     }
   }
-  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL>), dim3(grid),
+  hipLaunchKernelGGL((attention_kernel<D, FP8, HEAD, NQ, CAUSAL, SHARED>), dim3(grid),
                      dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
@@ -1293,6 +1430,8 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
 template <int D, bool FP8, bool HEAD>
 hipError_t launch_attention_q(const AttnArgs& a, hipStream_t s) {
   if (a.q_len == 1) return launch_attention_t<D, FP8, HEAD, 1, false>(a, s);
+  // prefill column blocks of kPrefillCols: the page-sharing kernel
+  if (a.col_blocks > 1 && kPrefillCols == 32) return launch_attention_t<D, FP8, HEAD, 2, true, true>(a, s);
   const int cols = a.group * a.q_len;
   if (cols <= 16) return launch_attention_t<D, FP8, HEAD, 1, true>(a, s);
   if (cols <= 32) return launch_attention_t<D, FP8, HEAD, 2, true>(a, s);

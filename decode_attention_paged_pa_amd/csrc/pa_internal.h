@@ -11,6 +11,12 @@ constexpr int kWaves = 4;          // waves (independent work items) per attenti
 constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
 constexpr int kMaxQLen = 8;        // query tokens per sequence in one multi-query call
 constexpr int kMaxCols = 64;       // query columns (heads x tokens) per unit: 4 MFMA tiles
+#ifndef PA_SHARED_PREFILL
+#define PA_SHARED_PREFILL 1        // prefill: 32-column waves that share each page through LDS
+#endif
+// Query columns per wave of a prefill chunk (units of more than kMaxCols
+// columns): 32 for the page-sharing kernel, else 64.
+constexpr int kPrefillCols = PA_SHARED_PREFILL ? 32 : kMaxCols;
 constexpr int kMassRun = 128;      // pages per wave of the eviction score pass (LDS rows)
 
 // Arguments of the attention (partial) kernel.

@@ -267,8 +267,11 @@ def test_prefill_arguments_and_partitions():
     assert pf(cl=2048 * 16 + 1) == -1                     # longer than the table holds
     assert pf(hq=8 * 17) == -2
     n = lambda cl, p: L.pa_prefill_num_partitions(ctypes.byref(c), ctypes.byref(s), 32, cl, p)  # noqa: E731
-    # 4 x 8 units x (4 heads x 2048 tokens / 64) column blocks = 4096 waves: no split
+    # page-sharing prefill: 4 x 8 units x (4 heads x 2048 tokens / 32 / 4) workgroups of
+    # four 32-column blocks = 2048 workgroups, above the 1536 aimed at: no split; a
+    # 512-token chunk gives 512 workgroups: 3 partitions
     assert n(2048, 0) == 1
+    assert n(512, 0) == 3
     # a short chunk gives few waves (32): the prefix is split into 64 partitions
     # of 32 pages (about 2048 waves, partitions no shorter than 32 pages)
     assert n(16, 0) == 64
