@@ -672,6 +672,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   f32x4 o[WIDE ? 1 : NQ][WIDE ? 1 : NT];
   f32x16 ow[NP][NJ];
   float m_run[NQ], l_acc[NQ];
+  float thr[NQ];   // m_run + kRescaleSlack: a page rescales when a score exceeds it
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     if constexpr (!WIDE) {
@@ -679,6 +680,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       for (int j = 0; j < NT; ++j) o[nq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     m_run[nq] = kEmptyMax;
+    thr[nq] = kEmptyMax + kRescaleSlack;
     l_acc[nq] = 0.f;
   }
   if constexpr (WIDE) {
@@ -849,7 +851,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       lmax[nq] = max4(sc[nq][0], sc[nq][1], sc[nq][2], sc[nq][3]);
-      grow |= lmax[nq] > m_run[nq] + kRescaleSlack;
+      grow |= lmax[nq] > thr[nq];
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
       float alph[NQ];
@@ -857,7 +859,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) {
         alph[nq] = 1.f;
-        moved[nq] = __builtin_amdgcn_ballot_w64(lmax[nq] > m_run[nq] + kRescaleSlack) != 0;
+        moved[nq] = __builtin_amdgcn_ballot_w64(lmax[nq] > thr[nq]) != 0;
         if (moved[nq]) {
           const float m_new = fmaxf(m_run[nq], col_max(lmax[nq]));
           const float alpha = __builtin_amdgcn_exp2f(m_run[nq] - m_new);
@@ -868,6 +870,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
           }
           alph[nq] = alpha;
           m_run[nq] = m_new;
+          thr[nq] = m_new + kRescaleSlack;
         }
       }
       if constexpr (WIDE) {   // lanes with (l & 16) hold the pair's second tile's column
@@ -886,7 +889,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[nq][r] - m_run[nq]);
-      l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
+      // (the page-sharing BF16 kernel sums the rounded weights it multiplies
+      // V by, two per dot instruction: its normaliser is then exactly the sum
+      // of the P operands)
+      if (!(SHARED && !FP8)) l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
       if (FP8) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) pbh[nq][r] = (_Float16)(p[r] * vsc);
@@ -896,6 +902,11 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         const bf16x2 hi = __builtin_convertvector(f32x2{p[2], p[3]}, bf16x2);
         pbb[nq] = __builtin_bit_cast(i16x4, u32x2{__builtin_bit_cast(uint32_t, lo),
                                                  __builtin_bit_cast(uint32_t, hi)});
+        if constexpr (SHARED) {
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          l_acc[nq] = __builtin_amdgcn_fdot2_f32_bf16(
+              hi, one, __builtin_amdgcn_fdot2_f32_bf16(lo, one, l_acc[nq], false), false);
+        }
       }
     }
 
@@ -1267,6 +1278,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
               for (int j = 0; j < NT; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
               m_run[0] = -INFINITY;
+              thr[0] = -INFINITY;
               l_acc[0] = 0.f;
             }
           }
