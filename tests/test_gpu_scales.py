@@ -3,8 +3,8 @@
 A negative scale reverses the ranking of the scores, zero makes the weights
 uniform over the attended tokens, and a large one makes them nearly one-hot.
 Each is checked against the fp64 oracle run with the same scale, for plain
-decode (fixed and balanced splits), 4 drafts and a short prefill chunk, BF16
-and FP8.  Bars: mean-abs 1e-3 everywhere, and per element max-abs 1e-2
+decode (fixed and balanced splits), 4 drafts and prefill chunks of 16, 40 and
+100 tokens, BF16 and FP8.  Bars: mean-abs 1e-3 everywhere, and per element max-abs 1e-2
 against the fp64 oracle -- except where the output's own BF16 step is coarser
 than that bar: with the sharp scale an output is close to one V row (|o| up to
 about 4), and one BF16 ulp is 2^-6 for |o| in [2, 4) and 2^-5 in [4, 8), so
@@ -62,9 +62,14 @@ def test_decode_scales(kv):
                    sharp=f > 1)
 
 
-@pytest.mark.parametrize("kv,T", [("fp8", 4), ("bf16", 16)])
+# 4 drafts; prefill chunks of 16 tokens (64 columns: one multi-query wave per
+# unit) and of 40 and 100 tokens (160 and 400 columns: the page-sharing kernel,
+# which applies the scale inside the exponential and takes the column extreme
+# from the raw scores, so the sign and zero of the scale are its own cases)
+@pytest.mark.parametrize("kv,T", [("fp8", 4), ("bf16", 16), ("bf16", 40), ("fp8", 100)])
 def test_multi_query_and_prefill_scales(kv, T):
-    w = make_workload(2, batch=3, lens=[20, 700, 2100], q_len=T, kv=kv, stale_frac=0.0)
+    w = make_workload(2, batch=3, lens=[max(20, T + 20), 700, 2100], q_len=T, kv=kv,
+                      stale_frac=0.0)
     dw = build_device_workload(w)
     dw.step_append()
     cache, _ = oracle_fill(w)
