@@ -214,9 +214,9 @@ Split mass_split(const pa_cache_desc* c, const pa_seq_desc* s) {
   return sp;
 }
 
-// Chunked prefill: a unit's G * T query columns go in blocks of 64, one wave
-// per block, so there are far more waves than units; split-K is only needed
-// when the grid would otherwise be small.
+// Chunked prefill: a unit's G * T query columns go in blocks of kPrefillCols
+// (32: four blocks per page-sharing workgroup), so there are far more waves
+// than units; split-K is only needed when the grid would otherwise be small.
 int prefill_col_blocks(const pa_cache_desc* c, int32_t hq, int32_t q_len) {
   const int64_t cols = (int64_t)(hq / c->num_kv_heads) * q_len;
   if (cols <= pa::kMaxCols) return 1;   // one multi-query wave holds the unit's columns

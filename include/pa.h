@@ -345,9 +345,12 @@ int pa_decode_step_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
  * chunk_len tokens of every unit (appended before the call); token t sees
  * tokens 0 .. lens[u] - chunk_len + t (the cached prefix and the chunk up to
  * itself).  q, out: device BF16 [B][chunk_len][Hq][D].
- * The query columns (heads x chunk tokens) of a unit go to waves in blocks of
- * 64; num_partitions (0 = automatic) splits the prefix only when the grid
- * would otherwise be small.  Workspace: pa_prefill_workspace_bytes(...).
+ * A unit's query columns (heads x chunk tokens) go to waves in blocks of 32,
+ * four blocks per workgroup, whose waves share each page of the unit (staged
+ * once through LDS); a unit of at most 64 columns is one multi-query wave.
+ * num_partitions (0 = automatic) splits the prefix only when the grid would
+ * otherwise be small (the automatic choice aims at about 1536 workgroups).
+ * Workspace: pa_prefill_workspace_bytes(...).
  */
 int pa_prefill(const pa_cache_desc *cache, const pa_seq_desc *seq, int32_t num_q_heads,
                int32_t chunk_len, const uint16_t *q, uint16_t *out, float softmax_scale,
