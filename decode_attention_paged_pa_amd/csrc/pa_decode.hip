@@ -401,9 +401,12 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(AppendArgs ap, int item
 // ------------------------------------------------------------- attention
 // One wave owns one work item = (unit, partition), unit = (sequence, KV
 // head), partition = a run of chunk_pages pages of the unit.  The four waves
-// of a workgroup are independent (no LDS, no barrier): each streams its pages
-// through a register ring and writes its own partial (max, sum, O) -- or, with
-// a single partition, the normalised output -- straight from registers.
+// of a workgroup are independent (no LDS ring, no barrier): each streams its
+// pages through a register ring and writes its own partial (max, sum, O) --
+// or, with a single partition, the normalised output -- straight from
+// registers.  The exception is the prefill kernel (SHARED): its four waves
+// are 32-column blocks of one unit that load each page once, into an LDS
+// ring, with a barrier per page (see the page loop).
 //
 // Query columns: the G query heads of the unit for each of its T query
 // tokens, column cc = t * G + g, in NQ tiles of 16.  T > 1 is a multi-query
@@ -457,8 +460,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   const int T = CAUSAL ? a.q_len : 1;
   const int C = G * T;                         // query columns of the unit
-  // Long chunks (prefill) split a unit's columns into blocks of 16 * NQ, one
-  // wave per block; a block reads only the pages its last column can see.
+  // Long chunks (prefill) split a unit's columns into blocks of 16 * NQ (32:
+  // the page-sharing kernel), one wave per block; a block reads (SHARED:
+  // computes) only the pages its last column can see.
   const int cblocks = a.col_blocks;
   // readfirstlane: the wave index is uniform, and saying so keeps every
   // per-page index, bound and branch in scalar registers.

@@ -7,7 +7,7 @@
 namespace pa {
 
 constexpr int kPageSize = 16;      // tokens per page (S)
-constexpr int kWaves = 4;          // waves (independent work items) per attention workgroup
+constexpr int kWaves = 4;          // waves per attention workgroup (independent work items but in prefill)
 constexpr int kMaxGroup = 16;      // query heads per KV head held in one MFMA tile
 constexpr int kMaxQLen = 8;        // query tokens per sequence in one multi-query call
 constexpr int kMaxCols = 64;       // query columns (heads x tokens) per unit: 4 MFMA tiles
@@ -40,7 +40,7 @@ struct AttnArgs {
   float* part_ml;            // [B][q_len][Hq][Pn][2] running max (log2 domain) and sum
   int batch, num_q_heads, num_kv_heads, group, table_width, num_pages;
   int q_len;                 // query tokens per sequence (1: decode; > 1: causal drafts)
-  int col_blocks;            // blocks of 64 query columns per unit (prefill chunks); else 1
+  int col_blocks;            // blocks of kPrefillCols query columns per unit (prefill chunks); else 1
   float* row_ml;             // scored decode: [B][Hq][2] final max (log2) and sum per row
   float* scores;             // eviction score pass: [P][Hkv (SEQ) or 1 (HEAD)][S] page scores
   int chunk_pages, num_parts;
