@@ -3,9 +3,12 @@
 The chunk's C tokens are the last C tokens of each unit; token t sees tokens
 0 .. L - C + t (oracle_decode_multi, pinned in test_oracle_multi.py).  Same
 bars as decode: BF16 outputs within max-abs 1e-2 / mean-abs 1e-3 of the fp64
-oracle, flags bit-exact, flagged rows +0.0.  Chunks span many 64-column
-blocks (one wave each); cases cover both layouts and dtypes, G up to 16,
-split prefixes, a prefix of zero, and a sampled check at a realistic size.
+oracle, flags bit-exact, flagged rows +0.0.  Chunks of more than 64 columns
+run on the page-sharing kernel: 32-column blocks, four per workgroup, sharing
+each page through LDS; the cases include workgroups whose last blocks lie past
+the unit's columns (132 and 291 columns: 1 and 2 of 4 waves without columns),
+both layouts and dtypes, D 64, G up to 16, split prefixes, a prefix of zero,
+and a sampled check at a realistic size.
 """
 import numpy as np
 import pytest
