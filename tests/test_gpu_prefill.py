@@ -6,7 +6,7 @@ bars as decode: BF16 outputs within max-abs 1e-2 / mean-abs 1e-3 of the fp64
 oracle, flags bit-exact, flagged rows +0.0.  Chunks of more than 64 columns
 run on the page-sharing kernel: 32-column blocks, four per workgroup, sharing
 each page through LDS; the cases include workgroups whose last blocks lie past
-the unit's columns (132 and 291 columns: 1 and 2 of 4 waves without columns),
+the unit's columns (132 and 291 columns: 3 and 2 of 4 waves without columns),
 both layouts and dtypes, D 64, G up to 16, split prefixes, a prefix of zero,
 and a sampled check at a realistic size.
 """
