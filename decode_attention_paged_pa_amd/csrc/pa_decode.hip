@@ -101,7 +101,11 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #ifndef PA_SHARED_STAGES
 #define PA_SHARED_STAGES 4     // LDS pages of the page-sharing kernel's ring (3 in flight)
 #endif
-static_assert(PA_SHARED_STAGES >= 3 && PA_SHARED_STAGES <= 6, "page-sharing ring");
+static_assert(PA_SHARED_STAGES == 2 || PA_SHARED_STAGES == 4,
+              "page-sharing ring: whole ring cycles per 64-page id chunk, within the LDS");
+// Word 3 of a raw buffer resource on CDNA: 32-bit data format (any nonzero
+// format enables the access; untyped loads ignore it), no swizzle.
+constexpr int kBufWord3 = 0x00020000;
 constexpr int kPipe = PA_PIPE_DEPTH;
 static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
 static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
@@ -706,6 +710,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   float v_ref = 0.f;   // FP8: the reference V scale of the P.V operands (uniform; see kPScale)
   const int scale_stride = HEAD ? 1 : Hkv;
   const int lane_off = (c * 4 + q4) * 16;
+  // The page-sharing BF16 kernel keeps V in its LDS ring in the order of the
+  // 32x32x16 A operand (see its ring loads): each lane reads its operand as
+  // two 8-byte halves and no row swaps are needed.
+  constexpr bool VPERM = SHARED && !FP8;
 
   // Page ids, one lane per page, 512 pages (8 registers) at a time.  They are
   // loaded, and waited for, before the page loop of each 512-page segment:
@@ -918,7 +926,17 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     // slots may hold anything, and 0 * NaN would poison the sum)
     if (page * kPageSize + kPageSize > L) {   // the last page only, in place
       const int nv = min(max(L - tok0, 0), 4);  // this lane's valid tokens (4 per dword row)
-      if (FP8) {
+      if constexpr (VPERM) {
+        // operand order: tokens 8 h .. 8 h + 3 in dwords 0-1, 8 h + 4 .. 8 h + 7
+        // in dwords 2-3 (h = q4 >> 1), two tokens per dword, low half first
+        const int t0 = page * kPageSize + 8 * (q4 >> 1);
+        const int na = min(max(L - t0, 0), 4), nb = min(max(L - t0 - 4, 0), 4);
+        const uint64_t ma = na >= 4 ? ~0ull : ((1ull << (16 * na)) - 1ull);
+        const uint64_t mb = nb >= 4 ? ~0ull : ((1ull << (16 * nb)) - 1ull);
+        const u32x4 mk{(uint32_t)ma, (uint32_t)(ma >> 32), (uint32_t)mb, (uint32_t)(mb >> 32)};
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) vr[i] &= mk;
+      } else if (FP8) {
         const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
 #pragma unroll
         for (int i = 0; i < NSEG; ++i) vr[i] &= u32x4{m, m, m, m};
@@ -946,6 +964,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         if (FP8) {
           av = pair_rows(fp8x4_to_f16x4(vr[(2 * jj) >> 2][(2 * jj) & 3]),
                          fp8x4_to_f16x4(vr[(2 * jj + 1) >> 2][(2 * jj + 1) & 3]));
+        } else if constexpr (VPERM) {   // already in operand order
+          av = vr[jj];
         } else {   // tiles 2 jj and 2 jj + 1 are the two halves of segment jj
           const u32x4& seg = vr[jj];
           av = pair_rows(u32x2{seg[0], seg[1]}, u32x2{seg[2], seg[3]});
@@ -1138,13 +1158,26 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       // (the counter runs in order: only later pages' may stay in flight),
       // then a barrier makes the stage whole for all and proves that every
       // wave has read the previous page, whose stage the next request
-      // reuses.  Each lane requests the chunk that the compute lane of its
-      // index reads, so the LDS reads are linear.  Every wave runs all of
-      // the workgroup's pages (m: uniform) and computes those its own
-      // columns see (mw).
+      // reuses.  Every wave runs all of the workgroup's pages (m: uniform)
+      // and computes those its own columns see (mw).
+      //
+      // The loads are buffer loads: the segment's address is a scalar
+      // resource and the lane's offset a loop-invariant register, so a
+      // request costs no vector instructions.  A K lane fetches the chunk
+      // that the compute lane of its index reads (linear LDS reads).  A V
+      // lane L fetches chunk g = 4 (L & 15) + 2 ((L >> 4) & 1) + (L >> 5):
+      // the compute lane (c, q4) then finds its 32x32x16 A operand (chunks
+      // (c, 2 h) and (c, 2 h + 1), dwords 2 (q4 & 1) and 2 (q4 & 1) + 1,
+      // h = q4 >> 1) as two 8-byte words 512 bytes apart, and each half-wave
+      // reads 256 contiguous bytes.
+      //
+      // The pages run in 64-page chunks, one register of ids each: inside a
+      // chunk the ids stay put (the look-ahead page's id comes from this
+      // chunk's register or the next one's) and they shift once per chunk.
       constexpr int SEGS = 2 * NSEG;
       constexpr int MY = (SEGS + kWaves - 1) / kWaves;   // segments per wave and page
       constexpr int R = kStages;
+      static_assert(64 % R == 0, "a 64-page chunk holds whole ring cycles");
       auto ring = [&](auto st) -> u32x4 (*)[64] {
         constexpr int S = decltype(st)::value;
         if constexpr (S == 0) return s_st0;
@@ -1154,10 +1187,17 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         else if constexpr (S == 4) return s_st4;
         else return s_st5;
       };
+      const int v_off = VPERM ? ((lane & 15) * 4 + ((lane >> 4) & 1) * 2 + (lane >> 5)) * 16 : lane_off;
+      const int v_rd = ((q4 >> 1) * 16 + c) * 2 + (q4 & 1);   // 8-byte word of the V operand
       float stk[R], stv[R];   // FP8 scales of the pages in the ring
-      auto request = [&](auto st, int r) {   // page r into stage st
+      // page rr (of this chunk, or of the next one: nxt) into stage st
+      auto request = [&](auto st, int rr, bool nxt) {
         constexpr int S = decltype(st)::value;
-        const int pid = page_id(r);
+        const int l = rr & 63;
+        const int i0 = __builtin_amdgcn_readlane(ids[0], l);
+        const int i1 = __builtin_amdgcn_readlane(ids[1], l);
+        int pid = nxt ? i1 : i0;
+        pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
         const uint8_t* kp = kpool + (size_t)pid * page_stride;
         const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
         const uint8_t* vp = vpool + (size_t)vpid * page_stride;
@@ -1166,15 +1206,21 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         for (int i = 0; i < MY; ++i) {
           const int sg = wave + i * kWaves;
           if (sg < SEGS) {
-            const uint8_t* src = (sg < NSEG ? kp + sg * 1024 : vp + (sg - NSEG) * 1024) + lane_off;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)src,
-                (__attribute__((address_space(3))) void*)&dst[sg][0], 16, 0, 0);
+            const uint8_t* sp = sg < NSEG ? kp + sg * 1024 : vp + (sg - NSEG) * 1024;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sp), (short)0, 1024, kBufWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)&dst[sg][0], 16,
+                sg < NSEG ? lane_off : v_off, 0, 0, 0);
           }
         }
         if constexpr (SEGSC) {
-          stk[S] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), r & 63));
-          stv[S] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), r & 63));
+          const float k0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), l));
+          const float k1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[1]), l));
+          const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), l));
+          const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[1]), l));
+          stk[S] = nxt ? k1 : k0;
+          stv[S] = nxt ? v1 : v0;
         }
       };
       // every wave's reads of the ring are done (lgkmcnt), then the barrier;
@@ -1190,7 +1236,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       auto first = [&](auto jc) {   // pages 0 .. R - 2 into stages 0 .. R - 2
         constexpr int J = decltype(jc)::value;
         if constexpr (J + 1 < R) {
-          if (J < m) request(IntC<J>{}, J);
+          if (J < m) request(IntC<J>{}, J, false);
         }
       };
       first(IntC<0>{});
@@ -1198,34 +1244,52 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       first(IntC<2>{});
       first(IntC<3>{});
       first(IntC<4>{});
-      for (int r0 = 0; r0 < m; r0 += R) {
-        auto step = [&](auto uc) {
-          constexpr int U = decltype(uc)::value;
-          const int r = r0 + U;
-          if (r >= m) return;
-          // pages requested after page r: r + 1 .. min(r + R - 2, m - 1)
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          if (r + R - 2 < m) __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));  // vmcnt
-          else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
-          sync();
-          if (r + R - 1 < m) request(IntC<(U + R - 1) % R>{}, r + R - 1);
-          if (r < mw) {
-            u32x4 (*src)[64] = ring(IntC<U>{});
-            u32x4 kp[NSEG], vp[NSEG];
+      for (int c0 = 0; c0 < m; c0 += 64) {
+        const int ce = min(c0 + 64, m);
+        for (int r0 = c0; r0 < ce; r0 += R) {
+          auto step = [&](auto uc) {
+            constexpr int U = decltype(uc)::value;
+            const int r = r0 + U;
+            if (r >= ce) return;
+            // pages requested after page r: r + 1 .. min(r + R - 2, m - 1)
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (r + R - 2 < m) __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));  // vmcnt
+            else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
+            sync();
+            const int rr = r + R - 1;
+            if (rr < m) request(IntC<(U + R - 1) % R>{}, rr, rr - c0 >= 64);
+            if (r < mw) {
+              u32x4 (*src)[64] = ring(IntC<U>{});
+              u32x4 kp[NSEG], vp[NSEG];
 #pragma unroll
-            for (int i = 0; i < NSEG; ++i) {
-              kp[i] = src[i][lane];
-              vp[i] = src[NSEG + i][lane];
+              for (int i = 0; i < NSEG; ++i) {
+                kp[i] = src[i][lane];
+                if constexpr (VPERM) {
+                  const u32x2* vb = reinterpret_cast<const u32x2*>(&src[NSEG + i][0]) + v_rd;
+                  const u32x2 x = vb[0], y = vb[64];
+                  vp[i] = u32x4{x.x, x.y, y.x, y.y};
+                } else {
+                  vp[i] = src[NSEG + i][lane];
+                }
+              }
+              compute(kp, vp, stk[U], stv[U], seg + r);
             }
-            compute(kp, vp, stk[U], stv[U], seg + r);
+          };
+          step(IntC<0>{});
+          step(IntC<1>{});
+          if constexpr (R > 2) step(IntC<2>{});
+          if constexpr (R > 3) step(IntC<3>{});
+          if constexpr (R > 4) step(IntC<4>{});
+          if constexpr (R > 5) step(IntC<5>{});
+        }
+#pragma unroll
+        for (int t = 0; t + 1 < kIdRegs; ++t) {
+          ids[t] = ids[t + 1];
+          if constexpr (SEGSC) {
+            sks[t] = sks[t + 1];
+            svs[t] = svs[t + 1];
           }
-        };
-        step(IntC<0>{});
-        step(IntC<1>{});
-        step(IntC<2>{});
-        if constexpr (R > 3) step(IntC<3>{});
-        if constexpr (R > 4) step(IntC<4>{});
-        if constexpr (R > 5) step(IntC<5>{});
+        }
       }
       continue;
     }
