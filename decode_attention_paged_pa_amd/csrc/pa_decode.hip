@@ -106,6 +106,31 @@ static_assert(PA_SHARED_STAGES == 2 || PA_SHARED_STAGES == 4,
 // Word 3 of a raw buffer resource on CDNA: 32-bit data format (any nonzero
 // format enables the access; untyped loads ignore it), no swizzle.
 constexpr int kBufWord3 = 0x00020000;
+
+// One 1 KiB block from global memory straight into LDS: lane l fetches the
+// 16 bytes at src + voff (voff < 1024; the buffer's bounds return zeros past
+// the block) and they land at LDS byte lds + 16 l.  Written in asm so that
+// the compiler does not track it: its own tracking loses, at a loop's back
+// edge, which LDS buffer each load in flight writes, and then waits for every
+// load before the loop's first LDS read.  The caller orders the loads
+// against the LDS reads itself (s_waitcnt vmcnt, then a barrier).  The asm
+// has no destination register; M0 (the LDS base) is restored before it ends,
+// and the s_nop is the wait state an M0 write needs before an LDS-DMA load.
+__device__ inline void dma_block(const uint8_t* src, uint32_t lds, int voff) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t p = reinterpret_cast<uint64_t>(src);
+  const i32x4 rs{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), 1024, kBufWord3};
+  int keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
 constexpr int kPipe = PA_PIPE_DEPTH;
 static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
 static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
@@ -1161,8 +1186,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       // reuses.  Every wave runs all of the workgroup's pages (m: uniform)
       // and computes those its own columns see (mw).
       //
-      // The loads are buffer loads: the segment's address is a scalar
-      // resource and the lane's offset a loop-invariant register, so a
+      // The loads are buffer loads (dma_block): the segment's address is a
+      // scalar resource and the lane's offset a loop-invariant register, so a
       // request costs no vector instructions.  A K lane fetches the chunk
       // that the compute lane of its index reads (linear LDS reads).  A V
       // lane L fetches chunk g = 4 (L & 15) + 2 ((L >> 4) & 1) + (L >> 5):
@@ -1207,11 +1232,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
           const int sg = wave + i * kWaves;
           if (sg < SEGS) {
             const uint8_t* sp = sg < NSEG ? kp + sg * 1024 : vp + (sg - NSEG) * 1024;
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sp), (short)0, 1024, kBufWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)&dst[sg][0], 16,
-                sg < NSEG ? lane_off : v_off, 0, 0, 0);
+            dma_block(sp, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&dst[sg][0],
+                      sg < NSEG ? lane_off : v_off);
           }
         }
         if constexpr (SEGSC) {
