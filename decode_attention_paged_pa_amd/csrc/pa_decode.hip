@@ -132,8 +132,8 @@ __device__ inline void dma_block(const uint8_t* src, uint32_t lds, int voff) {
       : "memory");
 }
 constexpr int kPipe = PA_PIPE_DEPTH;
-static_assert(kPipe >= 2 && kPipe <= 6, "pipeline depth");
-static_assert(PA_MQ_PIPE_DEPTH >= 2 && PA_MQ_PIPE_DEPTH <= 6, "pipeline depth");
+static_assert(kPipe == 2 || kPipe == 4, "pipeline depth: whole ring cycles per 64-page id chunk");
+static_assert(PA_MQ_PIPE_DEPTH == 2 || PA_MQ_PIPE_DEPTH == 4, "pipeline depth: whole ring cycles per 64-page id chunk");
 
 // BF16 pages hold twice the bytes in the register ring, so that kernel gets
 // one wave per SIMD less than the FP8 one instead of spilling; every extra
@@ -159,6 +159,16 @@ __device__ inline u32x4 load16(const uint8_t* p) {
 #else
   return *reinterpret_cast<const u32x4*>(p);
 #endif
+}
+
+// 16 bytes at blk + soff + voff, through a buffer resource over the block:
+// blk and soff are uniform (scalar registers) and voff is the lane's offset,
+// so the address costs no vector instructions.  bytes bounds the access
+// (reads past it return zeros).
+__device__ inline u32x4 load_blk(const uint8_t* blk, int bytes, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), (short)0, bytes, kBufWord3);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, PA_NT_LOADS ? 2 : 0));
 }
 
 // ------------------------------------------------------------ validation
@@ -760,44 +770,57 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   constexpr int kSegPages = 64 * kIdRegs;
   int ids[kIdRegs];
   float sks[SEGSC ? kIdRegs : 1], svs[SEGSC ? kIdRegs : 1];
-  int id_chunk = 0;      // the 64-page chunk of the segment that ids[0] holds
-  auto page_id = [&](int r) {  // r: page index within the segment, uniform, non-decreasing
-    if ((r >> 6) != id_chunk) {
-#pragma unroll
-      for (int t = 0; t + 1 < kIdRegs; ++t) {
-        ids[t] = ids[t + 1];
-        if constexpr (SEGSC) {
-          sks[t] = sks[t + 1];
-          svs[t] = svs[t + 1];
-        }
-      }
-      ++id_chunk;
-    }
-    const int pid = __builtin_amdgcn_readlane(ids[0], r & 63);
+  // The id of page rr of the segment: rr lies in the 64-page chunk that
+  // ids[0] holds, or in the next one (nxt).  The loops walk the pages in
+  // 64-page chunks and shift the registers down by one after each
+  // (shift_ids): a shift under a condition inside the page loop made the
+  // compiler copy every id register on every page.  Each loop consumes W
+  // pages per iteration and loads W - 1 pages ahead, so only the steps
+  // u >= 1 of a chunk's last iteration load from the next chunk, and only
+  // when another chunk follows: that iteration runs after the chunk's loop.
+  // (nxt is a compile-time choice: the loops know which steps look into the
+  // next chunk, so no register is selected at run time)
+  auto pid_of = [&](int rr, auto nxt) __attribute__((always_inline)) {
+    const int pid = __builtin_amdgcn_readlane(ids[decltype(nxt)::value], rr & 63);
     return (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
   };
+  auto scale_of = [&](const float (&sv)[SEGSC ? kIdRegs : 1], int rr, auto nxt) __attribute__((always_inline)) {
+    constexpr int t = SEGSC ? decltype(nxt)::value : 0;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[t]), rr & 63));
+  };
+  auto shift_ids = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t + 1 < kIdRegs; ++t) {
+      ids[t] = ids[t + 1];
+      if constexpr (SEGSC) {
+        sks[t] = sks[t + 1];
+        svs[t] = svs[t + 1];
+      }
+    }
+  };
+  static_assert(kIdRegs >= 2, "a look-ahead page may sit in the next chunk");
 
-  // Page k's block: a scalar base address plus this lane's 16-byte chunk, so
+  // Page r's block: a scalar base address plus this lane's 16-byte chunk, so
   // that every load is one 1 KiB contiguous wave access.  FP8 scales of the
-  // page are requested with its data.
-  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int r) {
-    const int pid = page_id(r);
+  // page are requested with its data.  nxt: as for pid_of.
+  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int r, auto nxt) __attribute__((always_inline)) {
+    const int pid = pid_of(r, nxt);
     const uint8_t* kp = kpool + (size_t)pid * page_stride;
     const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
     const uint8_t* vp = vpool + (size_t)vpid * page_stride;
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
-      kr[i] = load16(kp + lane_off + i * 1024);
-      vr[i] = load16(vp + lane_off + i * 1024);
+      kr[i] = load_blk(kp, NSEG * 1024, lane_off, i * 1024);
+      vr[i] = load_blk(vp, NSEG * 1024, lane_off, i * 1024);
     }
     if constexpr (SEGSC) {   // vsc: the page's V scale / v_ref * kPScale
-      ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), r & 63));
-      vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), r & 63));
+      ksc = scale_of(sks, r, nxt);
+      vsc = scale_of(svs, r, nxt);
     }
   };
 
   // S^T of one page: acc[nq] = K Q^T for column tile nq (unscaled)
-  auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NSEG]) {
+  auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NSEG]) __attribute__((always_inline)) {
     // Q operand of tile nq, step st; the LDS index carries a per-page zero the
     // compiler cannot see through, so the reads are not hoisted out of the
     // page loop (which would put Q back into registers)
@@ -859,7 +882,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   };
 
   // Softmax update and O^T += V^T P^T for page k of the run, from its scores.
-  auto pv = [&](const f32x4 (&acc)[NQ], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
+  auto pv = [&](const f32x4 (&acc)[NQ], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) __attribute__((always_inline)) {
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ksc;
@@ -1027,7 +1050,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  auto compute = [&](const u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) {
+  auto compute = [&](const u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) __attribute__((always_inline)) {
     f32x4 acc[NQ];
     qk(acc, kr);
     pv(acc, vr, ksc, vsc, k);
@@ -1038,7 +1061,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // A column that saw no token (multi-query, L - T + t < 0) has sum 0 and
   // O = 0, and is written as zeros.  vfac converts O to the values' units
   // (FP8: v_ref / kPScale; 1 for BF16 and for a parked partition).
-  auto emit = [&](int part, float vfac) {
+  auto emit = [&](int part, float vfac) __attribute__((always_inline)) {
     if constexpr (WIDE) {
       float lt[NQ];
 #pragma unroll
@@ -1174,7 +1197,6 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
       for (int j = 0; j < kIdRegs; ++j) svs[j] *= to_op;
     }
-    id_chunk = 0;
     if constexpr (SHARED) {
       // The workgroup's waves load each page once, into LDS, for all of
       // them: wave w requests 1 KiB segments w, w + kWaves, ... of the page
@@ -1216,13 +1238,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       const int v_rd = ((q4 >> 1) * 16 + c) * 2 + (q4 & 1);   // 8-byte word of the V operand
       float stk[R], stv[R];   // FP8 scales of the pages in the ring
       // page rr (of this chunk, or of the next one: nxt) into stage st
-      auto request = [&](auto st, int rr, bool nxt) {
+      auto request = [&](auto st, int rr, auto nxt) __attribute__((always_inline)) {
         constexpr int S = decltype(st)::value;
-        const int l = rr & 63;
-        const int i0 = __builtin_amdgcn_readlane(ids[0], l);
-        const int i1 = __builtin_amdgcn_readlane(ids[1], l);
-        int pid = nxt ? i1 : i0;
-        pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+        const int pid = pid_of(rr, nxt);
         const uint8_t* kp = kpool + (size_t)pid * page_stride;
         const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
         const uint8_t* vp = vpool + (size_t)vpid * page_stride;
@@ -1237,17 +1255,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
           }
         }
         if constexpr (SEGSC) {
-          const float k0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[0]), l));
-          const float k1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sks[1]), l));
-          const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[0]), l));
-          const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svs[1]), l));
-          stk[S] = nxt ? k1 : k0;
-          stv[S] = nxt ? v1 : v0;
+          stk[S] = scale_of(sks, rr, nxt);
+          stv[S] = scale_of(svs, rr, nxt);
         }
       };
       // every wave's reads of the ring are done (lgkmcnt), then the barrier;
       // the compiler-only fences keep LDS accesses on their side of it
-      auto sync = [&]() {
+      auto sync = [&]() __attribute__((always_inline)) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0xC07F);               // s_waitcnt lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
@@ -1255,10 +1269,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       };
       const int mw = min(max(nw - seg, 0), m);
       sync();                                             // the last segment's reads are done
-      auto first = [&](auto jc) {   // pages 0 .. R - 2 into stages 0 .. R - 2
+      auto first = [&](auto jc) __attribute__((always_inline)) {   // pages 0 .. R - 2 into stages 0 .. R - 2
         constexpr int J = decltype(jc)::value;
         if constexpr (J + 1 < R) {
-          if (J < m) request(IntC<J>{}, J, false);
+          if (J < m) request(IntC<J>{}, J, IntC<0>{});
         }
       };
       first(IntC<0>{});
@@ -1268,8 +1282,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       first(IntC<4>{});
       for (int c0 = 0; c0 < m; c0 += 64) {
         const int ce = min(c0 + 64, m);
-        for (int r0 = c0; r0 < ce; r0 += R) {
-          auto step = [&](auto uc) {
+        // iter: the R pages from r0; lc: the last iteration of a chunk that
+        // another follows, whose steps u >= 1 load from the next chunk
+        auto iter = [&](const int r0, auto lc) __attribute__((always_inline)) {
+          auto step = [&](auto uc, auto lc) __attribute__((always_inline)) {
             constexpr int U = decltype(uc)::value;
             const int r = r0 + U;
             if (r >= ce) return;
@@ -1279,7 +1295,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
             sync();
             const int rr = r + R - 1;
-            if (rr < m) request(IntC<(U + R - 1) % R>{}, rr, rr - c0 >= 64);
+            if (rr < m) request(IntC<(U + R - 1) % R>{}, rr, IntC<(decltype(lc)::value && U >= 1) ? 1 : 0>{});
             if (r < mw) {
               u32x4 (*src)[64] = ring(IntC<U>{});
               u32x4 kp[NSEG], vp[NSEG];
@@ -1297,84 +1313,105 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
               compute(kp, vp, stk[U], stv[U], seg + r);
             }
           };
-          step(IntC<0>{});
-          step(IntC<1>{});
-          if constexpr (R > 2) step(IntC<2>{});
-          if constexpr (R > 3) step(IntC<3>{});
-          if constexpr (R > 4) step(IntC<4>{});
-          if constexpr (R > 5) step(IntC<5>{});
-        }
-#pragma unroll
-        for (int t = 0; t + 1 < kIdRegs; ++t) {
-          ids[t] = ids[t + 1];
-          if constexpr (SEGSC) {
-            sks[t] = sks[t + 1];
-            svs[t] = svs[t + 1];
-          }
-        }
+          step(IntC<0>{}, lc);
+          step(IntC<1>{}, lc);
+          if constexpr (R > 2) step(IntC<2>{}, lc);
+          if constexpr (R > 3) step(IntC<3>{}, lc);
+        };
+        const bool more = c0 + 64 < m;
+        int r0 = c0;
+        for (; r0 < (more ? ce - R : ce); r0 += R) iter(r0, IntC<0>{});
+        if (more) iter(r0, IntC<1>{});
+        shift_ids();
       }
       continue;
     }
     if constexpr (LATEK) {
       // One K buffer: page r+1 is requested as soon as page r's Q.K has read
       // K, and the waits are the compiler's (K before Q.K, V before P.V)
-      load(kr[0], vr[0], ks[0], vs[0], 0);
-      for (int r0 = 0; r0 < m; r0 += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = r0 + u;
-          if (r < m) {
-            f32x4 acc[NQ];
-            qk(acc, kr[0]);
-            if (r + 1 < m) load(kr[0], vr[1 - u], ks[1 - u], vs[1 - u], r + 1);
-            pv(acc, vr[u], ks[u], vs[u], seg + r);
-          }
-        }
+      load(kr[0], vr[0], ks[0], vs[0], 0, IntC<0>{});
+      for (int c0 = 0; c0 < m; c0 += 64) {
+        const int ce = min(c0 + 64, m);
+        auto iter = [&](const int r0, auto lc) __attribute__((always_inline)) {
+          auto step = [&](auto uc, auto lc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            const int r = r0 + u;
+            if (r < ce) {
+              f32x4 acc[NQ];
+              qk(acc, kr[0]);
+              if (r + 1 < m)
+                load(kr[0], vr[1 - u], ks[1 - u], vs[1 - u], r + 1,
+                     IntC<(decltype(lc)::value && u >= 1) ? 1 : 0>{});
+              pv(acc, vr[u], ks[u], vs[u], seg + r);
+            }
+          };
+          step(IntC<0>{}, lc);
+          step(IntC<1>{}, lc);
+        };
+        const bool more = c0 + 64 < m;
+        int r0 = c0;
+        for (; r0 < (more ? ce - 2 : ce); r0 += 2) iter(r0, IntC<0>{});
+        if (more) iter(r0, IntC<1>{});
+        shift_ids();
       }
       continue;
     }
+    static_assert(64 % PIPE == 0, "a 64-page chunk holds whole ring cycles");
 #pragma unroll
-    for (int u = 0; u < PIPE - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1));
-    for (int r0 = 0; r0 < m; r0 += PIPE) {
-#pragma unroll
-      for (int u = 0; u < PIPE; ++u) {
-        const int r = r0 + u;                      // page within the segment
-        const int slot = (u + PIPE - 1) % PIPE;  // a constant once the loop is unrolled
-        if constexpr (THROTTLE) {
-          // At most one page in flight per wave besides the one being consumed:
-          // measured on MI355X, 2048 waves each keeping two or more pages of
-          // random 2 KiB blocks outstanding move the cache 2-4% slower.
-          __builtin_amdgcn_s_waitcnt(0x0F70);      // s_waitcnt vmcnt(0)
-        }
-        load(kr[slot], vr[slot], ks[slot], vs[slot], min(r + PIPE - 1, m - 1));
-        if (r < m) {
-          const int k = seg + r;                   // page within this wave's run
-          if constexpr (NQ == 1) {
-            if (k == next_boundary) {
-              // Park the finished partition in LDS: a global store now would
-              // be waited for by the next page's throttle, and under the full
-              // read stream stores take long to complete (measured: 6% of the
-              // kernel time on the 32K-token FP8 workload).  FP8 O is parked in
-              // the values' units: the reference scale may still grow.
-              const float vfac = FP8 ? v_ref / kPScale : 1.f;
-#pragma unroll
-              for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[0][j][r] * vfac;
-              stash[4 * NT][lane] = m_run[0];
-              stash[4 * NT + 1][lane] = l_acc[0];
-              ++part;
-              next_boundary += chunk;
-#pragma unroll
-              for (int j = 0; j < NT; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-              m_run[0] = -INFINITY;
-              thr[0] = -INFINITY;
-              l_acc[0] = 0.f;
-            }
+    for (int u = 0; u < PIPE - 1; ++u) load(kr[u], vr[u], ks[u], vs[u], min(u, m - 1), IntC<0>{});
+    for (int c0 = 0; c0 < m; c0 += 64) {
+      const int ce = min(c0 + 64, m);
+      auto iter = [&](const int r0, auto lc) __attribute__((always_inline)) {
+        auto step = [&](auto uc, auto lc) __attribute__((always_inline)) {
+          constexpr int u = decltype(uc)::value;
+          const int r = r0 + u;                      // page within the segment
+          const int slot = (u + PIPE - 1) % PIPE;  // a constant once the loop is unrolled
+          if constexpr (THROTTLE) {
+            // At most one page in flight per wave besides the one being consumed:
+            // measured on MI355X, 2048 waves each keeping two or more pages of
+            // random 2 KiB blocks outstanding move the cache 2-4% slower.
+            __builtin_amdgcn_s_waitcnt(0x0F70);      // s_waitcnt vmcnt(0)
           }
-          compute(kr[u], vr[u], ks[u], vs[u], k);
-        }
-      }
+          const int rr = min(r + PIPE - 1, m - 1);
+          load(kr[slot], vr[slot], ks[slot], vs[slot], rr, IntC<(decltype(lc)::value && u >= 1) ? 1 : 0>{});
+          if (r < ce) {
+            const int k = seg + r;                   // page within this wave's run
+            if constexpr (NQ == 1) {
+              if (k == next_boundary) {
+                // Park the finished partition in LDS: a global store now would
+                // be waited for by the next page's throttle, and under the full
+                // read stream stores take long to complete (measured: 6% of the
+                // kernel time on the 32K-token FP8 workload).  FP8 O is parked in
+                // the values' units: the reference scale may still grow.
+                const float vfac = FP8 ? v_ref / kPScale : 1.f;
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) stash[4 * j + r][lane] = o[0][j][r] * vfac;
+                stash[4 * NT][lane] = m_run[0];
+                stash[4 * NT + 1][lane] = l_acc[0];
+                ++part;
+                next_boundary += chunk;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                m_run[0] = -INFINITY;
+                thr[0] = -INFINITY;
+                l_acc[0] = 0.f;
+              }
+            }
+            compute(kr[u], vr[u], ks[u], vs[u], k);
+          }
+        };
+        step(IntC<0>{}, lc);
+        step(IntC<1>{}, lc);
+        if constexpr (PIPE > 2) step(IntC<2>{}, lc);
+        if constexpr (PIPE > 3) step(IntC<3>{}, lc);
+      };
+      const bool more = c0 + 64 < m;
+      int r0 = c0;
+      for (; r0 < (more ? ce - PIPE : ce); r0 += PIPE) iter(r0, IntC<0>{});
+      if (more) iter(r0, IntC<1>{});
+      shift_ids();
     }
   }
   emit(part, FP8 ? v_ref / kPScale : 1.f);
@@ -1664,7 +1701,7 @@ __global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
 
   u32x4 kr[PIPE][NSEG];
   float ks[PIPE];
-  auto load = [&](int slot, int r) {   // r: page within the run, uniform
+  auto load = [&](int slot, int r) __attribute__((always_inline)) {   // r: page within the run, uniform
     const int raw = __builtin_amdgcn_readlane(lane_reg(ids, r), r & 63);
     const int pid = (unsigned)raw < (unsigned)a.num_pages ? raw : 0;
     const uint8_t* kp = kpool + (size_t)pid * page_stride;
@@ -1678,7 +1715,7 @@ __global__ __launch_bounds__(256) void mass_kernel(AttnArgs a) {
   __shared__ f32x4 s_mass[kWaves][kMassRun][4];
   f32x4 (*mass)[4] = s_mass[wave];
 
-  auto compute = [&](int slot, int k) {
+  auto compute = [&](int slot, int k) __attribute__((always_inline)) {
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ks[slot];
