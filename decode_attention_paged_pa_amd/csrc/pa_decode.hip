@@ -765,6 +765,11 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // then 256 pages, so that ids and scales fit the register budget.  The
   // segment's largest V scale updates the wave's reference scale there.
   constexpr bool SEGSC = FP8;
+  // FP8 kernels with several column tiles apply a page's V operand factor
+  // inside the exponent, exp2(s - (m - log2 f)) = f exp2(s - m), instead of
+  // one multiply per weight; the row sums take the weights back with one
+  // multiply-add by 1/f per tile.
+  constexpr bool VFOLD = FP8 && NQ >= 2;
   // (four-tile BF16 kernels keep fewer ids, for registers to read Q ahead)
   constexpr int kIdRegs = SEGSC ? 4 : (NQ == 4 ? PA_IDREGS4 : 8);
   constexpr int kSegPages = 64 * kIdRegs;
@@ -813,7 +818,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       kr[i] = load_blk(kp, NSEG * 1024, lane_off, i * 1024);
       vr[i] = load_blk(vp, NSEG * 1024, lane_off, i * 1024);
     }
-    if constexpr (SEGSC) {   // vsc: the page's V scale / v_ref * kPScale
+    if constexpr (SEGSC) {   // vsc: the page's V scale / v_ref * kPScale (VFOLD: its log2)
       ksc = scale_of(sks, r, nxt);
       vsc = scale_of(svs, r, nxt);
     }
@@ -886,6 +891,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ksc;
+    const float vinv = VFOLD ? __builtin_amdgcn_exp2f(-vsc) : 1.f;   // 1/f
     // lane (c, q4) holds the scores of column c of each tile for tokens 4*q4 + r
     const int tok0 = page * kPageSize + q4 * 4;
     const bool tail = page * kPageSize + kPageSize > vis_min;
@@ -947,15 +953,17 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       float p[4];
+      const float mq = VFOLD ? m_run[nq] - vsc : m_run[nq];   // (VFOLD: vsc = log2 f)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[nq][r] - m_run[nq]);
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[nq][r] - mq);
       // (the page-sharing BF16 kernel sums the rounded weights it multiplies
       // V by, two per dot instruction: its normaliser is then exactly the sum
       // of the P operands)
-      if (!(SHARED && !FP8)) l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
+      if constexpr (VFOLD) l_acc[nq] = __builtin_fmaf((p[0] + p[1]) + (p[2] + p[3]), vinv, l_acc[nq]);
+      else if (!(SHARED && !FP8)) l_acc[nq] += (p[0] + p[1]) + (p[2] + p[3]);
       if (FP8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pbh[nq][r] = (_Float16)(p[r] * vsc);
+        for (int r = 0; r < 4; ++r) pbh[nq][r] = (_Float16)(VFOLD ? p[r] : p[r] * vsc);
       } else {
         // two values per conversion (round to nearest even, as one by one)
         const bf16x2 lo = __builtin_convertvector(f32x2{p[0], p[1]}, bf16x2);
@@ -1195,7 +1203,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       }
       const float to_op = v_ref > 0.f ? kPScale / v_ref : 0.f;
 #pragma unroll
-      for (int j = 0; j < kIdRegs; ++j) svs[j] *= to_op;
+      for (int j = 0; j < kIdRegs; ++j) {
+        svs[j] *= to_op;
+        // (VFOLD: the exponent offset log2 of the factor, at least -64: a page
+        // 2^64 times below the segment's largest V contributes nothing
+        // measurable; a NaN factor stays NaN)
+        if constexpr (VFOLD) svs[j] = __builtin_amdgcn_logf(fmaxf(svs[j], 0x1p-64f) + (svs[j] - svs[j]));
+      }
     }
     if constexpr (SHARED) {
       // The workgroup's waves load each page once, into LDS, for all of
