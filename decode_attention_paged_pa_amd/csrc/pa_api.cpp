@@ -25,6 +25,9 @@ int check_cache(const pa_cache_desc* c) {
   if (c->num_pages <= 0 || c->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
   if (c->page_size != pa::kPageSize) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // the kernels form page offsets with 32-bit page strides
+  const int64_t esz = c->kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
+  if ((int64_t)c->num_kv_heads * c->page_size * c->head_dim * esz > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if (!c->k_pages || !c->v_pages) return PA_ERR_INVALID_ARG;
   if (!aligned(c->k_pages, 256) || !aligned(c->v_pages, 256)) return PA_ERR_INVALID_ARG;
   if (c->kv_dtype == PA_KV_FP8_E4M3) {

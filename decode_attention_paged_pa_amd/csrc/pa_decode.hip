@@ -506,6 +506,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // readfirstlane: the wave index is uniform, and saying so keeps every
   // per-page index, bound and branch in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < kWaves);   // workgroups of kWaves waves (launch bound)
   int b, h, g, cb = 0;  // sequence, KV head, partition group, column block of this wave
   int chunk = a.chunk_pages;
   bool direct = Pn == 1;   // no reduce follows for this wave's unit: it writes the output rows
@@ -786,8 +787,13 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // (nxt is a compile-time choice: the loops know which steps look into the
   // next chunk, so no register is selected at run time)
   auto pid_of = [&](int rr, auto nxt) __attribute__((always_inline)) {
-    const int pid = __builtin_amdgcn_readlane(ids[decltype(nxt)::value], rr & 63);
-    return (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    return __builtin_amdgcn_readlane(ids[decltype(nxt)::value], rr & 63);
+  };
+  // Byte offset of page pid's block in a pool: ids are non-negative and the
+  // page stride is below 2^31 (checked on the host), so one 32 x 32-bit
+  // multiply with a 64-bit product.
+  auto page_off = [&](int pid) __attribute__((always_inline)) {
+    return (uint64_t)(uint32_t)pid * (uint32_t)page_stride;
   };
   auto scale_of = [&](const float (&sv)[SEGSC ? kIdRegs : 1], int rr, auto nxt) __attribute__((always_inline)) {
     constexpr int t = SEGSC ? decltype(nxt)::value : 0;
@@ -810,9 +816,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // page are requested with its data.  nxt: as for pid_of.
   auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int r, auto nxt) __attribute__((always_inline)) {
     const int pid = pid_of(r, nxt);
-    const uint8_t* kp = kpool + (size_t)pid * page_stride;
+    const uint8_t* kp = kpool + page_off(pid);
     const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
-    const uint8_t* vp = vpool + (size_t)vpid * page_stride;
+    const uint8_t* vp = vpool + page_off(vpid);
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       kr[i] = load_blk(kp, NSEG * 1024, lane_off, i * 1024);
@@ -1169,6 +1175,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     // wait for the ids here, once per segment (see above)
     int last = __builtin_amdgcn_readfirstlane(ids[kIdRegs - 1]);
     asm volatile("" : : "s"(last));
+    // ids out of range (only possible with the tag check off) read page 0,
+    // so that no access leaves the pool
+#pragma unroll
+    for (int j = 0; j < kIdRegs; ++j) ids[j] = (unsigned)ids[j] < (unsigned)a.num_pages ? ids[j] : 0;
     if constexpr (SEGSC) {
 #pragma unroll
       for (int j = 0; j < kIdRegs; ++j) {
@@ -1255,9 +1265,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       auto request = [&](auto st, int rr, auto nxt) __attribute__((always_inline)) {
         constexpr int S = decltype(st)::value;
         const int pid = pid_of(rr, nxt);
-        const uint8_t* kp = kpool + (size_t)pid * page_stride;
+        const uint8_t* kp = kpool + page_off(pid);
         const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
-        const uint8_t* vp = vpool + (size_t)vpid * page_stride;
+        const uint8_t* vp = vpool + page_off(vpid);
         u32x4 (*dst)[64] = ring(st);
 #pragma unroll
         for (int i = 0; i < MY; ++i) {
@@ -1283,11 +1293,12 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       };
       const int mw = min(max(nw - seg, 0), m);
       sync();                                             // the last segment's reads are done
+      // Every step requests a page (past the segment's end, its last page
+      // again: an L2 hit into a stage nobody reads), so that the count of
+      // loads issued after page r's is always the same and one wait serves.
       auto first = [&](auto jc) __attribute__((always_inline)) {   // pages 0 .. R - 2 into stages 0 .. R - 2
         constexpr int J = decltype(jc)::value;
-        if constexpr (J + 1 < R) {
-          if (J < m) request(IntC<J>{}, J, IntC<0>{});
-        }
+        if constexpr (J + 1 < R) request(IntC<J>{}, min(J, m - 1), IntC<0>{});
       };
       first(IntC<0>{});
       first(IntC<1>{});
@@ -1303,13 +1314,12 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             constexpr int U = decltype(uc)::value;
             const int r = r0 + U;
             if (r >= ce) return;
-            // pages requested after page r: r + 1 .. min(r + R - 2, m - 1)
+            // requested after page r: the R - 2 steps' worth that follow it
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (r + R - 2 < m) __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));  // vmcnt
-            else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));   // vmcnt
             sync();
-            const int rr = r + R - 1;
-            if (rr < m) request(IntC<(U + R - 1) % R>{}, rr, IntC<(decltype(lc)::value && U >= 1) ? 1 : 0>{});
+            request(IntC<(U + R - 1) % R>{}, min(r + R - 1, m - 1),
+                    IntC<(decltype(lc)::value && U >= 1) ? 1 : 0>{});
             if (r < mw) {
               u32x4 (*src)[64] = ring(IntC<U>{});
               u32x4 kp[NSEG], vp[NSEG];
@@ -1338,6 +1348,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         if (more) iter(r0, IntC<1>{});
         shift_ids();
       }
+      // the last requests (repeats) land before the stages are used again or
+      // the workgroup's LDS is released
+      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
       continue;
     }
     if constexpr (LATEK) {

@@ -92,7 +92,8 @@ enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 /* OCP E4M3 ("fn"): max 448, no inf */
 enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad enum */
-  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, page_size not 16, GQA group > 16 */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, page_size not 16, GQA group > 16,
+                              a page of all KV heads (Hkv x 16 x D x bytes) of 2^31 bytes or more */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pa_decode_workspace_bytes */
   PA_ERR_LAUNCH = -4,      /* the HIP runtime refused a kernel launch */
   PA_ERR_SCRATCH = -5      /* pa_decode_noalloc: the call needs more than its static scratch */

@@ -129,6 +129,7 @@ def test_no_paging_window_matches_the_four_prompt_figure():
     (dict(page_size=32), -2), (dict(head_dim=96), -2), (dict(layout=5), -1),
     (dict(kv_dtype=3), -1), (dict(num_pages=0), -1), (dict(k_pages=None), -1),
     (dict(k_pages=FAKE + 8), -1), (dict(kv_dtype=1), -1),  # FP8 without scales
+    (dict(num_kv_heads=1 << 19), -2),   # a SEQ page row of 2^31 bytes: page strides are 32-bit
 ])
 def test_decode_rejects_bad_cache(kw, code):
     assert _decode(_cache(**kw), _seq()) == code
