@@ -709,7 +709,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // tiles), for the double-rate 32x32x16 P.V MFMA -- a page's 16 tokens are
   // exactly its K dimension (same register count: D / 2 per column tile).
   // In a 32 x 32 tile lane l holds column 32 p + (l & 31) and the dims
-  // 32 J + 8 g + 4 (l >> 5) + r of element 4 g + r.
+  // 32 J + 8 g + 4 (l >> 5) + r of element 4 g + r (VPERM: g = 1 and 3
+  // trade dims).
   constexpr bool WIDE = NQ >= 2;
   constexpr int NP = WIDE ? NQ / 2 : 1;        // column-tile pairs
   constexpr int NJ = WIDE ? NT / 2 : 1;        // 32-dim blocks
@@ -748,7 +749,11 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int lane_off = (c * 4 + q4) * 16;
   // The page-sharing BF16 kernel keeps V in its LDS ring in the order of the
   // 32x32x16 A operand (see its ring loads): each lane reads its operand as
-  // two 8-byte halves and no row swaps are needed.
+  // two 8-byte halves and no row swaps are needed.  Its P.V rows hold the
+  // dims in another order: row m = c + 16 b of a 32-dim block holds dim
+  // c + 16 (b ^ (c >> 3)), i.e. rows 8-15 and 24-31 trade places, so that
+  // the lanes of a 16-lane group read different halves of their LDS slots
+  // (emit maps the rows back).
   constexpr bool VPERM = SHARED && !FP8;
 
   // Page ids, one lane per page, 512 pages (8 registers) at a time.  They are
@@ -1099,7 +1104,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
                                   ((uint32_t)bf16_rne(v[4 * g + 1] * inv) << 16);
               const uint32_t hi = (uint32_t)bf16_rne(v[4 * g + 2] * inv) |
                                   ((uint32_t)bf16_rne(v[4 * g + 3] * inv) << 16);
-              *reinterpret_cast<u32x2*>(a.out + qrow * D + 32 * jj + 8 * g + dq) = u32x2{lo, hi};
+              *reinterpret_cast<u32x2*>(a.out + qrow * D + 32 * jj + 8 * (VPERM ? g ^ ((g & 1) << 1) : g) + dq) =
+                  u32x2{lo, hi};
             }
         } else {
           const size_t pi = planned ? (size_t)pslot * C + cc : qrow * Pn + part;
@@ -1110,7 +1116,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             for (int g = 0; g < 4; ++g) {
               const f32x16& v = ow[pp][jj];
               const f32x4 x = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-              *reinterpret_cast<f32x4*>(po + 32 * jj + 8 * g + dq) = FP8 ? x * vfac : x;
+              *reinterpret_cast<f32x4*>(po + 32 * jj + 8 * (VPERM ? g ^ ((g & 1) << 1) : g) + dq) =
+                  FP8 ? x * vfac : x;
             }
           if (dq == 0) {
             a.part_ml[pi * 2 + 0] = m_col;
@@ -1238,9 +1245,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       // that the compute lane of its index reads (linear LDS reads).  A V
       // lane L fetches chunk g = 4 (L & 15) + 2 ((L >> 4) & 1) + (L >> 5):
       // the compute lane (c, q4) then finds its 32x32x16 A operand (chunks
-      // (c, 2 h) and (c, 2 h + 1), dwords 2 (q4 & 1) and 2 (q4 & 1) + 1,
-      // h = q4 >> 1) as two 8-byte words 512 bytes apart, and each half-wave
-      // reads 256 contiguous bytes.
+      // (c, 2 h) and (c, 2 h + 1), the 8-byte half e = (q4 & 1) ^ (c >> 3) of
+      // each, h = q4 >> 1) as two 8-byte words 512 bytes apart.  Each 16-lane
+      // group reads 8 first and 8 second halves of 16 slots: 16 distinct bank
+      // pairs in 128 bytes, no bank conflicts.
       //
       // The pages run in 64-page chunks, one register of ids each: inside a
       // chunk the ids stay put (the look-ahead page's id comes from this
@@ -1259,7 +1267,8 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         else return s_st5;
       };
       const int v_off = VPERM ? ((lane & 15) * 4 + ((lane >> 4) & 1) * 2 + (lane >> 5)) * 16 : lane_off;
-      const int v_rd = ((q4 >> 1) * 16 + c) * 2 + (q4 & 1);   // 8-byte word of the V operand
+      // 8-byte word of the V operand: half (q4 & 1) ^ (c >> 3) of the slot (see VPERM)
+      const int v_rd = ((q4 >> 1) * 16 + c) * 2 + ((q4 & 1) ^ (c >> 3));
       float stk[R], stv[R];   // FP8 scales of the pages in the ring
       // page rr (of this chunk, or of the next one: nxt) into stage st
       auto request = [&](auto st, int rr, auto nxt) __attribute__((always_inline)) {
