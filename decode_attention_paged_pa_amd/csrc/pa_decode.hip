@@ -837,13 +837,15 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 
   // S^T of one page: acc[nq] = K Q^T for column tile nq (unscaled)
   auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NSEG]) __attribute__((always_inline)) {
-    // Q operand of tile nq, step st; the LDS index carries a per-page zero the
-    // compiler cannot see through, so the reads are not hoisted out of the
-    // page loop (which would put Q back into registers)
-    int qz = 0;
-    if constexpr (QLDS) asm volatile("" : "+v"(qz));
+    // Q operand of tile nq, step st; the LDS address passes through an empty
+    // asm on every page, so the compiler cannot tell it is the same and does
+    // not hoist the reads out of the page loop (which would put Q back into
+    // registers), and the reads use it with immediate offsets
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    lds_bf16x8* qb = (lds_bf16x8*)&s_q[wave][0][lane];
+    if constexpr (QLDS) asm volatile("" : "+v"(qb));
     auto qv = [&](int nq, int st) -> bf16x8 {
-      if constexpr (QLDS) return s_q[wave][nq * NSTEP + st][lane + qz];
+      if constexpr (QLDS) return qb[(nq * NSTEP + st) * 64];
       else return qop[nq][st];
     };
     // K operand of step st (16 tokens x 32 dims): FP8 codes widened to bf16
