@@ -39,7 +39,8 @@ tokens (random positions) into spare pages, and reports its GB/s instead.
 --prefill C times a chunked-prefill step (append of a C-token chunk, then
 pa_prefill) on a Llama-3.1-8B-shaped BF16 layer: 4 sequences whose cached
 prefixes are 0, 2K, 8K and 30K tokens; it reports TFLOP/s against the MFMA
-bf16 peak.
+bf16 peak.  --prefill-kv fp8 runs the same step over an FP8 cache (the K and V
+pages widened to the bf16 / f16 MFMA operands in registers).
 """
 import argparse
 import hashlib
@@ -384,6 +385,8 @@ def main():
                     help="time compaction to this fraction of the tokens instead")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time a chunked-prefill step with this chunk length instead")
+    ap.add_argument("--prefill-kv", choices=("bf16", "fp8"), default="bf16",
+                    help="cache format of the --prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter scale)")
     ap.add_argument("--ceiling-only", action="store_true",
@@ -424,8 +427,10 @@ def main():
         return bench_compaction(args)
     if args.prefill > 0:
         C = args.prefill
-        w = make_workload(2, batch=len(PREFILL_PREFIXES), stale_frac=0.0, q_len=C,
-                          lens=np.array(PREFILL_PREFIXES) + C, table_width=2048)
+        prefill_name = "llama8b-prefill" if args.prefill_kv == "bf16" else "llama8b-fp8-prefill"
+        w = make_workload(2 if args.prefill_kv == "bf16" else 3, batch=len(PREFILL_PREFIXES),
+                          stale_frac=0.0, q_len=C, lens=np.array(PREFILL_PREFIXES) + C,
+                          table_width=2048)
     else:
         heads = None
         if args.kv_heads > 0:
@@ -578,9 +583,10 @@ def main():
             "value": round(step_tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "llama8b-prefill: B=4, Hq=32, Hkv=8, D=128, page 16, BF16 KV, "
+            "config": {"workload": "%s: B=4, Hq=32, Hkv=8, D=128, page 16, %s KV, "
                                    "SEQ layout, cached prefixes %s, chunk %d, %d partitions, tag "
-                                   "check %s" % (list(PREFILL_PREFIXES), T, n_parts,
+                                   "check %s" % (prefill_name, args.prefill_kv.upper(),
+                                                 list(PREFILL_PREFIXES), T, n_parts,
                                                  "on" if check else "off"),
                        "global_batch": w.B, "chunk_tokens": T},
             "flops_per_step": fl,
@@ -591,7 +597,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "attention_kernel", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": traffic_from_profile("llama8b-prefill-%d" % T, None)},
+                         "traffic": traffic_from_profile("%s-%d" % (prefill_name, T), None)},
             "cpu_baseline": None}), flush=True)
         return
     result = {

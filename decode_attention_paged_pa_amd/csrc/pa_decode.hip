@@ -103,6 +103,15 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #endif
 static_assert(PA_SHARED_STAGES == 2 || PA_SHARED_STAGES == 4,
               "page-sharing ring: whole ring cycles per 64-page id chunk, within the LDS");
+#ifndef PA_SHARED_STAGES_FP8
+#define PA_SHARED_STAGES_FP8 4 // FP8 pages of the page-sharing kernel's ring
+#endif
+#ifndef PA_SHARED_LEAD_FP8
+#define PA_SHARED_LEAD_FP8 3   // FP8 pages requested ahead of the one being widened
+#endif
+static_assert((PA_SHARED_STAGES_FP8 == 4 || PA_SHARED_STAGES_FP8 == 8) &&
+              PA_SHARED_LEAD_FP8 >= 1 && PA_SHARED_LEAD_FP8 <= PA_SHARED_STAGES_FP8 - 1,
+              "page-sharing FP8 ring: whole ring cycles per 64-page id chunk; a stage is widened before it is reused");
 // Word 3 of a raw buffer resource on CDNA: 32-bit data format (any nonzero
 // format enables the access; untyped loads ignore it), no swizzle.
 constexpr int kBufWord3 = 0x00020000;
@@ -486,11 +495,20 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // SHARED: a ring of pages (K then V, 1 KiB segments) for the workgroup,
   // one array per stage, so that the compiler tells the stages apart and
   // waits for a stage's loads only where that stage is read.
-  constexpr int kStages = SHARED ? PA_SHARED_STAGES : 1;
+  constexpr int kStages = SHARED ? (FP8 ? PA_SHARED_STAGES_FP8 : PA_SHARED_STAGES) : 1;
   constexpr int kRingSegs = SHARED ? 2 * NSEG : 1;
   __shared__ u32x4 s_st0[kRingSegs][64], s_st1[kStages > 1 ? kRingSegs : 1][64],
       s_st2[kStages > 2 ? kRingSegs : 1][64], s_st3[kStages > 3 ? kRingSegs : 1][64],
-      s_st4[kStages > 4 ? kRingSegs : 1][64], s_st5[kStages > 5 ? kRingSegs : 1][64];
+      s_st4[kStages > 4 ? kRingSegs : 1][64], s_st5[kStages > 5 ? kRingSegs : 1][64],
+      s_st6[kStages > 6 ? kRingSegs : 1][64], s_st7[kStages > 7 ? kRingSegs : 1][64];
+  // SHARED with an FP8 cache (CVT): each wave widens the FP8 segments it
+  // loaded, one page ahead, into the bf16 (K) and f16 (V) MFMA operands of
+  // every lane, in one of two buffers; the waves then read operands that
+  // need no conversion.  Per page: the 2 * NSEG operands of Q.K (one per
+  // 32-dim step), then the 2 * NSEG of P.V (one per 32-dim block).
+  constexpr bool CVT = SHARED && FP8;
+  constexpr int NOP = CVT ? 2 * NSEG : NSEG;   // operand registers per K (or V) of a page
+  __shared__ u32x4 s_cv0[CVT ? 2 * NOP : 1][64], s_cv1[CVT ? 2 * NOP : 1][64];
 
   const int Pn = a.num_parts;
   const bool planned = a.plan != nullptr;      // length-balanced split (see plan_block)
@@ -819,7 +837,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // Page r's block: a scalar base address plus this lane's 16-byte chunk, so
   // that every load is one 1 KiB contiguous wave access.  FP8 scales of the
   // page are requested with its data.  nxt: as for pid_of.
-  auto load = [&](u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float& ksc, float& vsc, int r, auto nxt) __attribute__((always_inline)) {
+  auto load = [&](u32x4 (&kr)[NOP], u32x4 (&vr)[NOP], float& ksc, float& vsc, int r, auto nxt) __attribute__((always_inline)) {
     const int pid = pid_of(r, nxt);
     const uint8_t* kp = kpool + page_off(pid);
     const int vpid = v_rot ? pid : ((pid ^ 1) < a.num_pages ? (pid ^ 1) : pid);
@@ -836,7 +854,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   };
 
   // S^T of one page: acc[nq] = K Q^T for column tile nq (unscaled)
-  auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NSEG]) __attribute__((always_inline)) {
+  auto qk = [&](f32x4 (&acc)[NQ], const u32x4 (&kr)[NOP]) __attribute__((always_inline)) {
     // Q operand of tile nq, step st; the LDS address passes through an empty
     // asm on every page, so the compiler cannot tell it is the same and does
     // not hoist the reads out of the page loop (which would put Q back into
@@ -849,8 +867,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       else return qop[nq][st];
     };
     // K operand of step st (16 tokens x 32 dims): FP8 codes widened to bf16
+    // (CVT: widened already)
     auto kv = [&](int st) -> bf16x8 {
-      if constexpr (FP8) {
+      if constexpr (FP8 && !CVT) {
         const int i = st >> 1, hh = st & 1;
         u32x2 lo = fp8x4_to_bf16x4(kr[i][2 * hh]);
         u32x2 hi = fp8x4_to_bf16x4(kr[i][2 * hh + 1]);
@@ -900,7 +919,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   };
 
   // Softmax update and O^T += V^T P^T for page k of the run, from its scores.
-  auto pv = [&](const f32x4 (&acc)[NQ], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) __attribute__((always_inline)) {
+  auto pv = [&](const f32x4 (&acc)[NQ], u32x4 (&vr)[NOP], float ksc, float vsc, int k) __attribute__((always_inline)) {
     const int page = p0 + k;
     float kfac = a.score_scale_log2;
     if (FP8) kfac *= ksc;
@@ -992,8 +1011,9 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
 
     // ---- O^T += V^T P^T; on the last page zero V of tokens past L (the
-    // slots may hold anything, and 0 * NaN would poison the sum)
-    if (page * kPageSize + kPageSize > L) {   // the last page only, in place
+    // slots may hold anything, and 0 * NaN would poison the sum; CVT: zeroed
+    // when widened)
+    if (!CVT && page * kPageSize + kPageSize > L) {   // the last page only, in place
       const int nv = min(max(L - tok0, 0), 4);  // this lane's valid tokens (4 per dword row)
       if constexpr (VPERM) {
         // operand order: tokens 8 h .. 8 h + 3 in dwords 0-1, 8 h + 4 .. 8 h + 7
@@ -1030,10 +1050,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
         u32x4 av;
-        if (FP8) {
+        if constexpr (FP8 && !CVT) {
           av = pair_rows(fp8x4_to_f16x4(vr[(2 * jj) >> 2][(2 * jj) & 3]),
                          fp8x4_to_f16x4(vr[(2 * jj + 1) >> 2][(2 * jj + 1) & 3]));
-        } else if constexpr (VPERM) {   // already in operand order
+        } else if constexpr (VPERM || CVT) {   // already in operand order
           av = vr[jj];
         } else {   // tiles 2 jj and 2 jj + 1 are the two halves of segment jj
           const u32x4& seg = vr[jj];
@@ -1071,7 +1091,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
     }
   };
 
-  auto compute = [&](const u32x4 (&kr)[NSEG], u32x4 (&vr)[NSEG], float ksc, float vsc, int k) __attribute__((always_inline)) {
+  auto compute = [&](const u32x4 (&kr)[NOP], u32x4 (&vr)[NOP], float ksc, float vsc, int k) __attribute__((always_inline)) {
     f32x4 acc[NQ];
     qk(acc, kr);
     pv(acc, vr, ksc, vsc, k);
@@ -1169,7 +1189,7 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   // (an L2 hit) so that every iteration issues the same loads.  At each
   // partition boundary the finished partition is emitted and the state
   // restarts; the ring keeps streaming across it.
-  u32x4 kr[PIPE][NSEG], vr[PIPE][NSEG];
+  u32x4 kr[PIPE][NOP], vr[PIPE][NOP];   // (NOP = NSEG on these paths)
   float ks[PIPE], vs[PIPE];
   int part = part0;
   int next_boundary = chunk;  // page index (relative to p0) of the next partition
@@ -1259,6 +1279,12 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       constexpr int MY = (SEGS + kWaves - 1) / kWaves;   // segments per wave and page
       constexpr int R = kStages;
       static_assert(64 % R == 0, "a 64-page chunk holds whole ring cycles");
+      // pages requested ahead of the one a step waits for: page r (CVT: page
+      // r + 1, which the step widens) may wait while LEAD later pages load.
+      // A stage is requested again once every wave (CVT: the wave that loaded
+      // it, the only one that reads it) has read it.
+      constexpr int LEAD = CVT ? PA_SHARED_LEAD_FP8 : R - 2;
+      static_assert(LEAD + (CVT ? 1 : 2) <= R, "a stage is read before it is requested again");
       auto ring = [&](auto st) -> u32x4 (*)[64] {
         constexpr int S = decltype(st)::value;
         if constexpr (S == 0) return s_st0;
@@ -1266,7 +1292,46 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
         else if constexpr (S == 2) return s_st2;
         else if constexpr (S == 3) return s_st3;
         else if constexpr (S == 4) return s_st4;
-        else return s_st5;
+        else if constexpr (S == 5) return s_st5;
+        else if constexpr (S == 6) return s_st6;
+        else return s_st7;
+      };
+      auto cvbuf = [&](auto bc) -> u32x4 (*)[64] {
+        if constexpr (decltype(bc)::value == 0) return s_cv0;
+        else return s_cv1;
+      };
+      // CVT: this wave's FP8 segments of page k (in ring stage st) widened
+      // into operand buffer bc: a K segment holds the 16-byte halves of two
+      // Q.K steps, a V segment the 4-token rows of two 32-dim P.V blocks
+      // (one row swap each, as the register path does).  V of tokens past L
+      // is zeroed first, on the unit's last page.
+      auto widen = [&](auto st, auto bc, int k) __attribute__((always_inline)) {
+        u32x4 (*src)[64] = ring(st);
+        u32x4 (*dst)[64] = cvbuf(bc);
+        const int page = p0 + k;
+#pragma unroll
+        for (int i = 0; i < MY; ++i) {
+          const int sg = wave + i * kWaves;
+          if (sg < NSEG) {
+            const u32x4 w = src[sg][lane];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const u32x2 lo = fp8x4_to_bf16x4(w[2 * hh]), hi = fp8x4_to_bf16x4(w[2 * hh + 1]);
+              dst[2 * sg + hh][lane] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+          } else if (sg < SEGS) {
+            u32x4 w = src[sg][lane];
+            if (page * kPageSize + kPageSize > L) {
+              const int nv = min(max(L - (page * kPageSize + q4 * 4), 0), 4);
+              const uint32_t mk = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+              w &= u32x4{mk, mk, mk, mk};
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              dst[NOP + 2 * (sg - NSEG) + hh][lane] =
+                  pair_rows(fp8x4_to_f16x4(w[2 * hh]), fp8x4_to_f16x4(w[2 * hh + 1]));
+          }
+        }
       };
       const int v_off = VPERM ? ((lane & 15) * 4 + ((lane >> 4) & 1) * 2 + (lane >> 5)) * 16 : lane_off;
       // 8-byte word of the V operand: half (q4 & 1) ^ (c >> 3) of the slot (see VPERM)
@@ -1307,15 +1372,23 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       // Every step requests a page (past the segment's end, its last page
       // again: an L2 hit into a stage nobody reads), so that the count of
       // loads issued after page r's is always the same and one wait serves.
-      auto first = [&](auto jc) __attribute__((always_inline)) {   // pages 0 .. R - 2 into stages 0 .. R - 2
+      auto first = [&](auto jc) __attribute__((always_inline)) {   // pages 0 .. LEAD into stages 0 .. LEAD
         constexpr int J = decltype(jc)::value;
-        if constexpr (J + 1 < R) request(IntC<J>{}, min(J, m - 1), IntC<0>{});
+        if constexpr (J <= LEAD) request(IntC<J>{}, min(J, m - 1), IntC<0>{});
       };
       first(IntC<0>{});
       first(IntC<1>{});
       first(IntC<2>{});
       first(IntC<3>{});
       first(IntC<4>{});
+      first(IntC<5>{});
+      first(IntC<6>{});
+      if constexpr (CVT) {
+        // page 0 widened before the loop; each step then widens the next
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (LEAD * MY));   // vmcnt: this wave's page 0
+        widen(IntC<0>{}, IntC<0>{}, seg);
+      }
       for (int c0 = 0; c0 < m; c0 += 64) {
         const int ce = min(c0 + 64, m);
         // iter: the R pages from r0; lc: the last iteration of a chunk that
@@ -1325,33 +1398,64 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
             constexpr int U = decltype(uc)::value;
             const int r = r0 + U;
             if (r >= ce) return;
-            // requested after page r: the R - 2 steps' worth that follow it
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | ((R - 2) * MY));   // vmcnt
-            sync();
-            request(IntC<(U + R - 1) % R>{}, min(r + R - 1, m - 1),
-                    IntC<(decltype(lc)::value && U >= 1) ? 1 : 0>{});
-            if (r < mw) {
-              u32x4 (*src)[64] = ring(IntC<U>{});
-              u32x4 kp[NSEG], vp[NSEG];
+            constexpr int nxt = (decltype(lc)::value && U + LEAD + 1 >= R) ? 1 : 0;
+            if constexpr (CVT) {
+              // The widened page r is whole after the barrier.  After page
+              // r's compute, this wave widens its FP8 segments of page r + 1
+              // (read once the LEAD later pages' loads, the one just
+              // requested included, are all that may remain), so that the
+              // conversions overlap the compute's last MFMAs.  (At the
+              // segment's last page the stage holds a repeat of it, widened
+              // into the buffer nobody reads.)  Page r's scales are read
+              // first: the request may reuse its stage.
+              const float ksc = stk[U], vsc = stv[U];
+              sync();
+              request(IntC<(U + LEAD + 1) % R>{}, min(r + LEAD + 1, m - 1), IntC<nxt>{});
+              if (r < mw) {
+                u32x4 (*src)[64] = cvbuf(IntC<U & 1>{});
+                u32x4 kp[NOP], vp[NOP];
 #pragma unroll
-              for (int i = 0; i < NSEG; ++i) {
-                kp[i] = src[i][lane];
-                if constexpr (VPERM) {
-                  const u32x2* vb = reinterpret_cast<const u32x2*>(&src[NSEG + i][0]) + v_rd;
-                  const u32x2 x = vb[0], y = vb[64];
-                  vp[i] = u32x4{x.x, x.y, y.x, y.y};
-                } else {
-                  vp[i] = src[NSEG + i][lane];
+                for (int i = 0; i < NOP; ++i) {
+                  kp[i] = src[i][lane];
+                  vp[i] = src[NOP + i][lane];
                 }
+                compute(kp, vp, ksc, vsc, seg + r);
               }
-              compute(kp, vp, stk[U], stv[U], seg + r);
+              __atomic_signal_fence(__ATOMIC_SEQ_CST);
+              __builtin_amdgcn_s_waitcnt(0x0F70 | (LEAD * MY));   // vmcnt
+              if (r + 1 < m) widen(IntC<(U + 1) % R>{}, IntC<(U + 1) & 1>{}, seg + r + 1);
+            } else {
+              // requested after page r: the LEAD steps' worth that follow it
+              __atomic_signal_fence(__ATOMIC_SEQ_CST);
+              __builtin_amdgcn_s_waitcnt(0x0F70 | (LEAD * MY));   // vmcnt
+              sync();
+              request(IntC<(U + LEAD + 1) % R>{}, min(r + LEAD + 1, m - 1), IntC<nxt>{});
+              if (r < mw) {
+                u32x4 (*src)[64] = ring(IntC<U>{});
+                u32x4 kp[NOP], vp[NOP];
+#pragma unroll
+                for (int i = 0; i < NSEG; ++i) {
+                  kp[i] = src[i][lane];
+                  if constexpr (VPERM) {
+                    const u32x2* vb = reinterpret_cast<const u32x2*>(&src[NSEG + i][0]) + v_rd;
+                    const u32x2 x = vb[0], y = vb[64];
+                    vp[i] = u32x4{x.x, x.y, y.x, y.y};
+                  } else {
+                    vp[i] = src[NSEG + i][lane];
+                  }
+                }
+                compute(kp, vp, stk[U], stv[U], seg + r);
+              }
             }
           };
           step(IntC<0>{}, lc);
           step(IntC<1>{}, lc);
           if constexpr (R > 2) step(IntC<2>{}, lc);
           if constexpr (R > 3) step(IntC<3>{}, lc);
+          if constexpr (R > 4) step(IntC<4>{}, lc);
+          if constexpr (R > 5) step(IntC<5>{}, lc);
+          if constexpr (R > 6) step(IntC<6>{}, lc);
+          if constexpr (R > 7) step(IntC<7>{}, lc);
         };
         const bool more = c0 + 64 < m;
         int r0 = c0;

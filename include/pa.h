@@ -348,7 +348,9 @@ int pa_decode_step_timed(const pa_cache_desc *cache, const pa_seq_desc *seq,
  * itself).  q, out: device BF16 [B][chunk_len][Hq][D].
  * A unit's query columns (heads x chunk tokens) go to waves in blocks of 32,
  * four blocks per workgroup, whose waves share each page of the unit (staged
- * once through LDS); a unit of at most 64 columns is one multi-query wave.
+ * once through LDS; an FP8 page is also widened to bf16 / f16 operands there
+ * once, each wave widening the quarter it loaded); a unit of at most 64
+ * columns is one multi-query wave.
  * num_partitions (0 = automatic) splits the prefix only when the grid would
  * otherwise be small (the automatic choice aims at about 1536 workgroups).
  * Workspace: pa_prefill_workspace_bytes(...).

@@ -9,7 +9,7 @@ after the chunk and segment edges (some with a partial last page), so that with
 one partition a unit's run ends at each of them, and with the automatic split
 the runs start past them.  Every kernel kind: one query (FP8, BF16), 4 drafts
 (two column tiles), 8 drafts (four tiles, FP8 and BF16) and a prefill chunk
-(the page-sharing kernel).  Bars as in the other parity tests.
+(the page-sharing kernel, BF16 and FP8).  Bars as in the other parity tests.
 """
 import pytest
 
@@ -36,9 +36,12 @@ def test_runs_at_chunk_and_segment_edges(cfg, q_len, kw):
     run_case(w, partitions=(1, 0))
 
 
-def test_prefill_runs_at_chunk_and_segment_edges():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_runs_at_chunk_and_segment_edges(kv):
     """The page-sharing kernel (128-token chunk of G 4: 512 columns, 16 blocks):
-    its ring requests run 3 pages ahead and cross the same edges."""
+    its ring requests run 3 pages ahead (BF16) or 2 pages ahead of the page
+    each wave widens, one page ahead of the one computed (FP8), and cross the
+    same edges."""
     lens = EDGE_LENS[:8] + [513 * 16 - 9]
-    w = make_workload(2, batch=len(lens), lens=lens, q_len=128, table_width=WIDTH)
+    w = make_workload(2, batch=len(lens), lens=lens, q_len=128, table_width=WIDTH, kv=kv)
     run_case(w, partitions=(1, 0))
