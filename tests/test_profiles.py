@@ -34,6 +34,11 @@ BENCH = _bench()
 def _algorithmic(name):
     """Algorithmic bytes per launch of the kernel a summary covers, from its workload name."""
     kind, wl = name.split("_", 2)[1:]
+    if wl.startswith("llama8b-fp8-prefill-"):
+        C = int(wl.rsplit("-", 1)[1])
+        w = make_workload(3, batch=len(BENCH.PREFILL_PREFIXES), stale_frac=0.0, q_len=C,
+                          lens=np.array(BENCH.PREFILL_PREFIXES) + C, table_width=2048)
+        return BENCH.algorithmic_bytes(w)["attention_kernel"]
     if wl.startswith("llama8b-prefill-"):
         C = int(wl.rsplit("-", 1)[1])
         w = make_workload(2, batch=len(BENCH.PREFILL_PREFIXES), stale_frac=0.0, q_len=C,
