@@ -8,7 +8,7 @@ run on the page-sharing kernel: 32-column blocks, four per workgroup, sharing
 each page through LDS; the cases include workgroups whose last blocks lie past
 the unit's columns (132 and 291 columns: 3 and 2 of 4 waves without columns),
 both layouts and dtypes, D 64, G up to 16, split prefixes, a prefix of zero,
-and a sampled check at a realistic size.
+and sampled checks at a realistic size (BF16 and FP8 caches).
 """
 import numpy as np
 import pytest
@@ -68,12 +68,15 @@ def test_prefill_short_chunks_equal_decode_multi_and_decode():
     assert torch.equal(c[:, 0].view(torch.int16), d.view(torch.int16))
 
 
-def test_prefill_realistic_size_sampled():
-    """Llama-3.1-8B-shaped BF16 layer, 4 sequences with prefixes 0, 2K, 8K, 30K and a
-    2048-token chunk: sampled rows against the oracle, all rows finite."""
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_realistic_size_sampled(kv):
+    """Llama-3.1-8B-shaped layer (BF16 or FP8 cache), 4 sequences with prefixes 0, 2K,
+    8K, 30K and a 2048-token chunk: sampled rows against the oracle, all rows finite.
+    (FP8: the page-sharing kernel widens each page once per workgroup, over 256-page
+    id segments.)"""
     C = 2048
     prefix = np.array([0, 2048, 8192, 30720])
-    w = make_workload(2, batch=4, lens=prefix + C, q_len=C, table_width=2048)
+    w = make_workload(2, batch=4, lens=prefix + C, q_len=C, table_width=2048, kv=kv)
     dw = build_device_workload(w, log=log)
     dw.step_append()
     out = pa.prefill(dw.cache, dw.q, dw.block_table, dw.lens, w.sigma,
@@ -95,5 +98,5 @@ def test_prefill_realistic_size_sampled():
                     ref, _ = attention_f64(bf16_to_f64(w.q[b, t, hq]), K[:n], V[:n], w.sigma)
                     errs.append(np.abs(got[b, t, hq] - ref))
     e = np.concatenate(errs)
-    log("prefill sampled: max-abs %.3g mean-abs %.3g over %d values" % (e.max(), e.mean(), e.size))
+    log("prefill sampled (%s): max-abs %.3g mean-abs %.3g over %d values" % (kv, e.max(), e.mean(), e.size))
     assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
