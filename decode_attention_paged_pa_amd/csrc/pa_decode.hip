@@ -99,7 +99,7 @@ __device__ inline float max4(float a, float b, float c, float d) {
 #define PA_SHARED_WAVES 3      // occupancy hint of the page-sharing kernel
 #endif
 #ifndef PA_SHARED_STAGES
-#define PA_SHARED_STAGES 4     // LDS pages of the page-sharing kernel's ring (3 in flight)
+#define PA_SHARED_STAGES 4     // LDS pages of the page-sharing BF16 kernel's ring (3 in flight)
 #endif
 static_assert(PA_SHARED_STAGES == 2 || PA_SHARED_STAGES == 4,
               "page-sharing ring: whole ring cycles per 64-page id chunk, within the LDS");
@@ -1260,6 +1260,15 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
       // wave has read the previous page, whose stage the next request
       // reuses.  Every wave runs all of the workgroup's pages (m: uniform)
       // and computes those its own columns see (mw).
+      //
+      // FP8 (CVT): the stages hold FP8 codes, and only the wave that loaded
+      // a segment reads it.  In page r's step each wave widens its segments
+      // of page r + 1 into the operand buffer that no wave reads in this
+      // step; the next step's barrier makes that buffer whole.  So a wave
+      // waits only for its own loads of page r + 1, a stage can be requested
+      // again once its loading wave has widened it (the requests run LEAD + 1
+      // pages ahead, up to kStages), and page r's scales are read before the
+      // step's request reuses their slot.
       //
       // The loads are buffer loads (dma_block): the segment's address is a
       // scalar resource and the lane's offset a loop-invariant register, so a
