@@ -140,11 +140,16 @@ def test_multi_query_magnitudes(T, heads):
 
 
 def test_prefill_chunk_magnitudes():
-    """A 96-token prefill chunk (4 column tiles, column blocks) over FP8 pages at
-    mixed magnitudes."""
+    """A 96-token prefill chunk (384 columns: the page-sharing kernel, FP8 pages
+    widened once per workgroup) over FP8 pages at mixed magnitudes, and with V
+    growing along units of up to 1024 pages, so that the waves' reference scale
+    grows at every 256-page segment while pages are widened one ahead."""
     w = make_workload(3, batch=2, lens=[700, 5000], q_len=96, stale_frac=0.0,
                       kv_mag={"v": ("pages", -3, 4)})
     run_range_case(w, partitions=(0,))
+    w = make_workload(3, batch=2, lens=[16384, 4500], q_len=96, stale_frac=0.0,
+                      kv_mag={"v": ("ramp", -4, 4)})
+    run_range_case(w, partitions=(0, 1))
 
 
 @pytest.mark.parametrize("D", [128, 64])
