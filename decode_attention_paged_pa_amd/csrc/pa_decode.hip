@@ -664,6 +664,10 @@ __global__ __launch_bounds__(256) PA_OCCUPANCY void attention_kernel(AttnArgs a)
   const int npages_w = !SHARED ? npages : (cend > cbase ? pages_to(cend) : 0);
   const int p0 = part0 * chunk;
   const int p1 = planned ? min(p0 + chunk, npages) : min(min(part0 + ppw, Pn) * chunk, npages);
+  // Fixed partitions: a unit whose pages all lie in its first partition has
+  // nothing to merge, so that partition's waves write its output rows and the
+  // reduce skips them (as for the planned split's single-partition groups).
+  if (!planned && part0 == 0 && npages_all <= chunk) direct = true;
   bool flagged;
   if (a.unit_flags != nullptr) {   // HEAD with the check: the sequence's unit words
     uint32_t word = 0u;
@@ -1637,7 +1641,9 @@ __global__ __launch_bounds__(PA_RED_THREADS) void reduce_kernel(AttnArgs a) {
     *reinterpret_cast<u32x2*>(orow) = u32x2{0u, 0u};
     return;
   }
-  if (a.plan != nullptr && nparts == 1) return;   // written by the attention kernel
+  // written by the attention kernel: a planned group's only partition, or a
+  // unit whose pages all lie in the first of the fixed partitions
+  if (a.plan != nullptr ? nparts == 1 : (L + kPageSize - 1) / kPageSize <= chunk) return;
   const float* ml = a.part_ml + pi0 * 2;
   const float* po = a.part_o + pi0 * D + d0;
   // Partitions in groups of 8 (16 for rows with more than 8), every load of a
