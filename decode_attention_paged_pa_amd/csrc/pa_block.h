@@ -72,7 +72,9 @@ __device__ __forceinline__ float bf16_value(uint16_t bits) { return __uint_as_fl
 // Every thread passes the FP8 path's one barrier exactly once, whether or not
 // its item writes anything (inactive items, items past the unit's last page,
 // unwritable pages), so items of different units may share a workgroup.
-template <int D, bool FP8, int NTH>
+// WHOLE compiles the FP8 path for whole pages written afresh (below); the
+// decode step's appends (a few tokens per unit) leave it out.
+template <int D, bool FP8, int NTH, bool WHOLE = true>
 __device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
                             float (&s_red)[2][NTH / 64], float (&s_old)[2]) {
 #pragma clang fp contract(off)
@@ -153,11 +155,53 @@ __device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
     uint8_t* kb = a.k_pages + blk * BLOCK_ELEMS;
     uint8_t* vb =
         a.v_pages + v_block_slot(pid, h, Hkv, a.num_pages, a.head_layout) * BLOCK_ELEMS;
+    // A whole page written afresh (slot 0, 16 tokens) from 16-byte aligned
+    // inputs, as bulk and chunk appends write them: the values are loaded 16
+    // bytes at a time and kept in registers across the barrier, and the codes
+    // go out as 8-byte K runs (8 dims of a token) and 4-byte V runs (4
+    // tokens of a dim).  Each element's arithmetic is the same as below.
+    const bool whole = WHOLE && cnt == kPageSize && slot0 == 0 &&
+                       ((reinterpret_cast<uintptr_t>(a.k_new) |
+                         reinterpret_cast<uintptr_t>(a.v_new)) & 15) == 0;
+    constexpr int KC = kPageSize * D / 8;            // K: 8 dims of a token each
+    constexpr int VC = (kPageSize / 4) * (D / 8);    // V: 4 tokens x 8 dims each
+    constexpr int KPT = (KC + NTH - 1) / NTH, VPT = (VC + NTH - 1) / NTH;
+    u32x4 kw[KPT], vw[VPT][4];
+    auto elem = [](const u32x4& w, int k) { return bf16_value((uint16_t)(w[k >> 1] >> (16 * (k & 1)))); };
     // amax of the new values, K and V separately
     float mk = 0.f, mv = 0.f;
-    for (int e = tid; e < cnt * D; e += NTH) {
-      mk = fmaxf(mk, fabsf(bf16_value(ks[e])));
-      mv = fmaxf(mv, fabsf(bf16_value(vs[e])));
+    if (whole) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int e = tid + i * NTH;
+        kw[i] = u32x4{0u, 0u, 0u, 0u};
+        if (e < KC) {
+          const int s = e / (D / 8), d = (e - s * (D / 8)) * 8;
+          kw[i] = *reinterpret_cast<const u32x4*>(ks + s * D + d);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mk = fmaxf(mk, fabsf(elem(kw[i], k)));
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int e = tid + i * NTH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vw[i][r] = u32x4{0u, 0u, 0u, 0u};
+        if (e < VC) {
+          const int tq = e / (D / 8), d0 = (e - tq * (D / 8)) * 8;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vw[i][r] = *reinterpret_cast<const u32x4*>(vs + (4 * tq + r) * D + d0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) mv = fmaxf(mv, fabsf(elem(vw[i][r], k)));
+      }
+    } else {
+      for (int e = tid; e < cnt * D; e += NTH) {
+        mk = fmaxf(mk, fabsf(bf16_value(ks[e])));
+        mv = fmaxf(mv, fabsf(bf16_value(vs[e])));
+      }
     }
     if (tid == 0 && cnt > 0) {
       s_old[0] = slot0 == 0 ? 0.f : a.k_scale[blk];  // a write at slot 0 starts the page afresh
@@ -185,6 +229,39 @@ __device__ void append_item(const AppendArgs& a, int item, bool active, int tid,
       const float amax = which ? mv : mk;
       const float cand = __fdiv_rn(amax, 448.0f);
       const float sn = so > cand ? so : cand;  // max(s_old, fl32(amax / 448))
+      auto code = [&](float x) -> uint32_t {
+        return sn == 0.f ? 0u : e4m3_rne_sat(__fdiv_rn(x, sn));
+      };
+      if (whole) {
+        if (which == 0) {
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            const int e = tid + i * NTH;
+            if (e >= KC) continue;
+            const int s = e / (D / 8), d = (e - s * (D / 8)) * 8;
+            uint32_t c[2] = {0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k >> 2] |= code(elem(kw[i], k)) << (8 * (k & 3));
+            *reinterpret_cast<u32x2*>(pb + k_elem<D, E>(s, d)) = u32x2{c[0], c[1]};
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < VPT; ++i) {
+            const int e = tid + i * NTH;
+            if (e >= VC) continue;
+            const int tq = e / (D / 8), d0 = (e - tq * (D / 8)) * 8;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              uint32_t c = 0u;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) c |= code(elem(vw[i][r], k)) << (8 * r);
+              *reinterpret_cast<uint32_t*>(pb + v_elem<D, E>(4 * tq, d0 + k)) = c;
+            }
+          }
+        }
+        if (tid == 0) (which ? a.v_scale : a.k_scale)[blk] = sn;
+        continue;
+      }
       if (sn > so && slot0 > 0) {
         for (int e = tid; e < slot0 * D; e += NTH) {
           const int t = e / D, d = e - t * D;

@@ -442,7 +442,7 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(AppendArgs ap, int item
   } else {
     const int qt = threadIdx.x >> 8;
     const int item = (x - nval - nplan) * 4 + qt;
-    append_item<D, FP8, 256>(ap, item, item < items, threadIdx.x & 255, s_red[qt], s_old[qt]);
+    append_item<D, FP8, 256, false>(ap, item, item < items, threadIdx.x & 255, s_red[qt], s_old[qt]);
   }
 }
 
