@@ -56,3 +56,18 @@ def test_prefill_workloads_share_their_flops():
     wf = make_workload(3, batch=len(lens), stale_frac=0.0, q_len=C, lens=lens, table_width=2048)
     assert wb.kv_dtype == "bf16" and wf.kv_dtype == "fp8"
     assert bench.prefill_flops(wb) == bench.prefill_flops(wf)
+
+
+def test_headline_attention_bytes_from_the_shape():
+    """The decode metric's bytes per attention launch on the 70B-shaped FP8 layer,
+    from its shape: K and V once (one byte per element), Q in BF16, the table
+    entries the step reads, and the K and V scales of every (page, KV head)."""
+    bench = _bench()
+    w = make_workload(5, stale_frac=0.0)
+    B, Hq, Hkv, D, L, S = 64, 64, 8, 128, 32768, 16
+    pages = L // S
+    kv = B * L * Hkv * 2 * D * 1
+    q = B * Hq * D * 2
+    table = B * pages * 4
+    scales = B * pages * Hkv * 2 * 4
+    assert bench.algorithmic_bytes(w)["attention_kernel"] == kv + q + table + scales == 4_304_928_768
