@@ -33,6 +33,8 @@ pytestmark = pytest.mark.gpu
     (2, dict(lens=np.array([[80, 300, 700, 1000, 90, 2000, 65, 64], [64, 100, 4000, 70, 99, 640, 300, 1000]]),
              kv="fp8", layout="head"), 64, (0, 2)),                       # FP8, HEAD
     (2, dict(batch=2, lens=[200, 1500], kv="fp8", head_dim=64), 100, (0, 2)),   # FP8, D 64
+    (2, dict(lens=np.array([[80, 700, 64, 1300, 99, 333, 65, 400], [1000, 64, 257, 90, 2048, 71, 640, 128]]),
+             kv="fp8", layout="head", head_dim=64), 48, (0, 3)),             # FP8, HEAD, D 64
 ])
 def test_prefill_matches_oracle(cfg, kw, C, parts):
     w = make_workload(cfg, q_len=C, **kw)
